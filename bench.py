@@ -1,0 +1,361 @@
+#!/usr/bin/env python3
+"""Benchmark of libswattn on one MI355X: prints ONE JSON line.
+
+A step is one forward + backward of causal attention on the "small" training
+workload (B8 H6 T2048 D128, bf16, full causal; seeded synthetic data), issued as
+the library's four kernels in order (forward, delta preprocess, dK/dV pass,
+dQ pass).  ``value`` is window-masked TFLOP/s of the whole step: forward
+4*D*N_vis*B*H, backward 2.5x that (the usual five-product accounting), with
+N_vis = sum_i min(i+1, W) visible (query, key) pairs per head.
+
+Also measured in the same run:
+* per-kernel average durations from HIP events recorded on the stream the
+  kernels run on, and the roofline of the dominant kernel;
+* KV-cache decode (32 sequences, H12 D128 bf16, lengths 512..4096 from seed 7;
+  full causal and window 1024) in HBM GB/s, cold cache (a 1 GiB buffer is
+  written before every timed call so the 256 MB MALL holds none of the cache);
+* the fp64 CPU oracle timed on a bounded sample of the same workload
+  (``cpu_baseline``).
+
+Only this file's ``cpu_baseline`` leg imports the oracle.
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (AMD public spec)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (AMD public spec)
+METRIC = "attn fwd+bwd TFLOP/s (masked FLOPs) and % bf16 MFMA peak; decode HBM GB/s"
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = sorted(glob.glob(os.path.join(ROOT, "causal_sliding_window_amd", "csrc", "*")))
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- accounting
+def visible_pairs(T: int, W: int) -> int:
+    """sum_{i<T} min(i+1, W): visible (query, key) pairs of one head."""
+    if W < 0 or W >= T:
+        return T * (T + 1) // 2
+    return W * (W + 1) // 2 + (T - W) * W
+
+
+def train_accounting(B, H, T, D, W, elem=2):
+    n = visible_pairs(T, W) * B * H
+    act = B * T * H * D * elem          # one [B,T,H,D] tensor
+    vec = B * H * T * 4                 # one [B,H,T] fp32 vector
+    return {
+        "pairs": n,
+        "flops_fwd": 4 * D * n,
+        "flops_bwd": 10 * D * n,
+        # algorithmic products per kernel: forward S, PV; dK/dV pass S, dP, dV, dK;
+        # dQ pass S, dP, dQ (2*D flops per visible pair each)
+        "kernel_flops": {"fwd": 4 * D * n, "bwd_dkdv": 8 * D * n, "bwd_dq": 6 * D * n,
+                         "bwd_pre": 2 * B * T * H * D},
+        # algorithmic HBM bytes per kernel: every operand read once, result written once
+        "kernel_bytes": {"fwd": 4 * act + vec, "bwd_pre": 2 * act + vec,
+                         "bwd_dkdv": 6 * act + 2 * vec, "bwd_dq": 5 * act + 2 * vec},
+    }
+
+
+def decode_bytes(lengths, H, D, W, elem=2):
+    vis = sum(min(int(L), W) if W > 0 else int(L) for L in lengths)
+    B = len(lengths)
+    return 2 * vis * H * D * elem + 2 * B * H * D * elem + B * H * 4
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        if p.endswith((".hip", ".h", ".cpp")):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------- GPU legs
+def bench_training(torch, swattn, inputs, cfg_name, steps, warmup):
+    c = inputs.CONFIGS[cfg_name]
+    B, H, T, D, W = c["B"], c["H"], c["T"], c["D"], c["windows"][0]
+    scale = 1.0 / math.sqrt(D)
+    x = {n: t.to("cuda:0") for n, t in inputs.config_inputs(cfg_name).items()}
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda:0")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(swattn.swattn_bwd_workspace_size(B, H, T, D), dtype=torch.uint8, device="cuda:0")
+    lib = swattn.lib()
+    P = swattn._ptr
+    stream = torch.cuda.current_stream()
+    sh = swattn.ctypes.c_void_p(stream.cuda_stream)
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {swattn.status_string(rc)}")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        check(lib.swattn_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, T, D, W, scale, sh), "fwd")
+        if ev is not None:
+            ev[1].record(stream)
+        check(lib.swattn_bwd_preprocess(P(o), P(do), P(ws), B, H, T, D, sh), "bwd_pre")
+        if ev is not None:
+            ev[2].record(stream)
+        check(lib.swattn_bwd_dkdv(P(q), P(k), P(v), P(do), P(lse), P(ws), P(dk), P(dv), B, H, T, D,
+                                  W, scale, sh), "bwd_dkdv")
+        if ev is not None:
+            ev[3].record(stream)
+        check(lib.swattn_bwd_dq(P(q), P(k), P(v), P(do), P(lse), P(ws), P(dq), B, H, T, D, W,
+                                scale, sh), "bwd_dq")
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"]
+    per = {n: statistics.fmean(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
+    return {"B": B, "H": H, "T": T, "D": D, "W": W, "wall_s": wall, "kernel_ms": per,
+            "acct": train_accounting(B, H, T, D, W)}
+
+
+def bench_decode(torch, swattn, inputs, iters):
+    c = inputs.CONFIGS["decode"]
+    d = inputs.config_inputs("decode")
+    lengths = d["seqlens"].tolist()
+    g = {n: t.to("cuda:0") for n, t in d.items()}
+    B, H, D, Tmax = c["B"], c["H"], c["D"], c["Tmax"]
+    scale = 1.0 / math.sqrt(D)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
+    out = {}
+    for W in c["windows"]:
+        ws = torch.empty(swattn.swattn_decode_workspace_size(B, H, D, Tmax, W), dtype=torch.uint8,
+                         device="cuda:0")
+        o = torch.empty_like(g["q"])
+        lse = torch.empty((B, H), dtype=torch.float32, device="cuda:0")
+
+        def call():
+            swattn.swattn_decode(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], o, lse, W, scale, ws)
+
+        for _ in range(3):
+            call()
+        cold, warm = [], []
+        for _ in range(iters):
+            flush.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        for _ in range(iters):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            warm.append(a.elapsed_time(b))
+        nbytes = decode_bytes(lengths, H, D, W)
+        ms = statistics.median(cold)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out["causal" if W < 0 else f"window{W}"] = {
+            "bytes": nbytes, "us_cold_median": round(ms * 1e3, 2),
+            "us_warm_median": round(statistics.median(warm) * 1e3, 2),
+            "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        }
+    return out
+
+
+# ----------------------------------------------------------------------------- CPU oracle leg
+def cpu_baseline(inputs, budget_s=12.0):
+    import numpy as np
+    from oracle import attention as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    c = inputs.CONFIGS["small"]
+    B, H, T, D, W = c["B"], c["H"], c["T"], c["D"], c["windows"][0]
+    x = inputs.config_inputs("small")
+    a = {n: inputs.to_f64(t) for n, t in x.items()}
+    scale = 1.0 / math.sqrt(D)
+    done, flops = 0, 0
+    t0 = time.perf_counter()
+    for b in range(B):
+        for h in range(H):
+            orc.head_fwd(a["q"][b, :, h], a["k"][b, :, h], a["v"][b, :, h], W, scale)
+            orc.head_bwd(a["q"][b, :, h], a["k"][b, :, h], a["v"][b, :, h], a["do"][b, :, h], W, scale)
+            done += 1
+            flops += 14 * D * visible_pairs(T, W)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        else:
+            continue
+        break
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {B * H} heads of the small workload (T={T}, D={D}, full causal): "
+                      f"NumPy fp64 oracle forward + backward, {el:.1f} s, same masked-FLOP count"}
+
+
+# ----------------------------------------------------------------------------- counters
+def traffic_for(kernel: str):
+    """HBM bytes per launch from stored rocprofv3 FETCH_SIZE/WRITE_SIZE counters, scaled by a
+    plain copy kernel's reading; None when missing or taken on different kernel sources."""
+    try:
+        data = json.load(open(COUNTERS))
+    except Exception:
+        return None
+    if data.get("source_hash") != source_hash():
+        return None
+    k = data.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return int(k["fetch_bytes"] * data["fetch_factor"] + k["write_bytes"] * data["write_factor"])
+
+
+def ingest_counters(fetch_csv, write_csv, copy_bytes):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into
+    profiles/counters.json.  The copy kernel (torch copy of `copy_bytes`) calibrates
+    each counter: factor = known bytes / counter bytes."""
+    import csv
+
+    def read(path, counter):
+        rows = {}
+        for r in csv.DictReader(open(path)):
+            if r.get("Counter_Name") != counter:
+                continue
+            rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: statistics.fmean(v) for k, v in rows.items()}
+
+    fe, wr = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
+    pick = lambda d, key: next((v for k, v in d.items() if key in k), None)  # noqa: E731
+    copy_f = pick(fe, "copy") or pick(fe, "elementwise")
+    copy_w = pick(wr, "copy") or pick(wr, "elementwise")
+    names = {"fwd": "fwd_bf16_kernel", "bwd_pre": "bwd_pre_bf16_kernel",
+             "bwd_dkdv": "bwd_dkdv_bf16_kernel", "bwd_dq": "bwd_dq_bf16_kernel",
+             "decode_split": "decode_split_kernel"}
+    out = {"source_hash": source_hash(), "copy_bytes": copy_bytes,
+           "fetch_factor": copy_bytes / copy_f if copy_f else 1.0,
+           "write_factor": copy_bytes / copy_w if copy_w else 1.0, "kernels": {}}
+    for n, sub in names.items():
+        f, w = pick(fe, sub), pick(wr, sub)
+        if f is not None and w is not None:
+            out["kernels"][n] = {"fetch_bytes": f, "write_bytes": w}
+    os.makedirs(os.path.dirname(COUNTERS), exist_ok=True)
+    json.dump(out, open(COUNTERS, "w"), indent=1)
+    print(json.dumps(out))
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="small", help="training workload (default: small)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-iters", type=int, default=20)
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="also run one torch copy of this many bytes (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"))
+    args = ap.parse_args()
+
+    if args.ingest_counters:
+        f, w, n = args.ingest_counters
+        ingest_counters(f, w, int(n))
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              f"multi-GPU path: run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    from causal_sliding_window_amd import inputs, swattn
+    if not torch.cuda.is_available():
+        print("no GPU visible: bench.py needs an MI355X", file=sys.stderr)
+        return 1
+    swattn.lib()  # fail loudly if the HIP library is missing
+
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    tr = bench_training(torch, swattn, inputs, args.config, args.steps, args.warmup)
+    acct = tr["acct"]
+    ms_step = tr["wall_s"] / args.steps * 1e3
+    flops_step = acct["flops_fwd"] + acct["flops_bwd"]
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    kernels = {}
+    for n, ms in tr["kernel_ms"].items():
+        f, by = acct["kernel_flops"][n], acct["kernel_bytes"][n]
+        kernels[n] = {"ms": round(ms, 4), "TFLOP_per_s": round(f / (ms * 1e-3) / 1e12, 1),
+                      "GB_per_s": round(by / (ms * 1e-3) / 1e9, 1)}
+    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: tr["kernel_ms"][n])
+    dom_ms = tr["kernel_ms"][dom]
+    achieved = acct["kernel_flops"][dom] / (dom_ms * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms, {value:.1f} TFLOP/s; kernels {kernels}")
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), RMS-normalised q/k)",
+        "config": {"workload": f"{args.config}: B{tr['B']} H{tr['H']} T{tr['T']} D{tr['D']} "
+                               f"window {tr['W']} bf16, forward + backward",
+                   "B": tr["B"], "H": tr["H"], "T": tr["T"], "D": tr["D"], "window": tr["W"],
+                   "parallelism": "none (1 GPU)"},
+        "pct_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels": kernels,
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for(dom),
+                     "algorithmic_bytes": acct["kernel_bytes"][dom]},
+    }
+    if not args.no_decode:
+        res["decode"] = bench_decode(torch, swattn, inputs, args.decode_iters)
+        log(f"decode {res['decode']}")
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inputs)
+        log(f"cpu baseline {res['cpu_baseline']}")
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

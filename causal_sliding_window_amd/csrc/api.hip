@@ -1,0 +1,249 @@
+// C ABI of libswattn (declared and documented in include/swattn.h).
+// Validates arguments, sizes workspaces and enqueues the kernels on the caller's
+// stream.  No allocation, no host synchronisation, no global state.
+#include <limits.h>
+#include <initializer_list>
+#include <stdint.h>
+
+#include "launch.h"
+#include "swattn.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int B, int H, int T, int D, int window) {
+  if (B <= 0 || H <= 0 || T <= 0 || D <= 0 || window == 0) return SWATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return SWATTN_ERR_UNSUPPORTED;
+  // kernels index rows of [B, T, H] and grid blocks with 32-bit ints
+  const long long rows = (long long)B * T * H;
+  if (rows > INT_MAX / 2 || (long long)B * H * ((T + 127) / 128) > INT_MAX / 2)
+    return SWATTN_ERR_INVALID_ARG;
+  return SWATTN_OK;
+}
+
+int all_aligned(std::initializer_list<const void *> ps) {
+  for (const void *p : ps)
+    if (p == nullptr || !aligned16(p)) return 0;
+  return 1;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SWATTN_OK : SWATTN_ERR_HIP; }
+
+int check_decode(int B, int H, int D, int Tmax, int window) {
+  if (B <= 0 || H <= 0 || D <= 0 || Tmax <= 0 || window == 0) return SWATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return SWATTN_ERR_UNSUPPORTED;
+  if ((long long)B * Tmax * H > INT_MAX / 2 || B > 65535 || H > 65535)
+    return SWATTN_ERR_INVALID_ARG;
+  return SWATTN_OK;
+}
+
+}  // namespace
+
+namespace swattn {
+
+hipError_t launch_bwd_pre(bool bf16, const void *o, const void *dO, float *delta, int B, int H,
+                          int T, int D, hipStream_t st) {
+  return bf16 ? launch_bwd_pre_bf16(o, dO, delta, B, H, T, D, st)
+              : launch_bwd_pre_f32((const float *)o, (const float *)dO, delta, B, H, T, D, st);
+}
+
+hipError_t launch_bwd_dkdv(bool bf16, const void *q, const void *k, const void *v,
+                           const void *dO, const float *lse, const float *delta, void *dk,
+                           void *dv, int B, int H, int T, int D, int window, float scale,
+                           hipStream_t st) {
+  if (bf16)
+    return launch_bwd_dkdv_bf16(q, k, v, dO, lse, delta, dk, dv, B, H, T, D, window, scale, st);
+  return launch_bwd_dkdv_f32((const float *)q, (const float *)k, (const float *)v,
+                             (const float *)dO, lse, delta, (float *)dk, (float *)dv, B, H, T, D,
+                             window, scale, st);
+}
+
+hipError_t launch_bwd_dq(bool bf16, const void *q, const void *k, const void *v, const void *dO,
+                         const float *lse, const float *delta, void *dq, int B, int H, int T,
+                         int D, int window, float scale, hipStream_t st) {
+  if (bf16) return launch_bwd_dq_bf16(q, k, v, dO, lse, delta, dq, B, H, T, D, window, scale, st);
+  return launch_bwd_dq_f32((const float *)q, (const float *)k, (const float *)v,
+                           (const float *)dO, lse, delta, (float *)dq, B, H, T, D, window, scale,
+                           st);
+}
+
+}  // namespace swattn
+
+namespace {
+
+int bwd_all(bool bf16, const void *q, const void *k, const void *v, const void *o,
+            const void *dO, const float *lse, void *dq, void *dk, void *dv, int B, int H, int T,
+            int D, int window, float scale, void *workspace, hipStream_t st) {
+  int s = check_common(B, H, T, D, window);
+  if (s != SWATTN_OK) return s;
+  if (!all_aligned({q, k, v, o, dO, dq, dk, dv, workspace}) || lse == nullptr)
+    return SWATTN_ERR_INVALID_ARG;
+  float *delta = (float *)workspace;
+  hipError_t e = swattn::launch_bwd_pre(bf16, o, dO, delta, B, H, T, D, st);
+  if (e == hipSuccess)
+    e = swattn::launch_bwd_dkdv(bf16, q, k, v, dO, lse, delta, dk, dv, B, H, T, D, window, scale,
+                                st);
+  if (e == hipSuccess)
+    e = swattn::launch_bwd_dq(bf16, q, k, v, dO, lse, delta, dq, B, H, T, D, window, scale, st);
+  return hip_status(e);
+}
+
+int bwd_pre(bool bf16, const void *o, const void *dO, void *workspace, int B, int H, int T, int D,
+            hipStream_t st) {
+  int s = check_common(B, H, T, D, -1);
+  if (s != SWATTN_OK) return s;
+  if (!all_aligned({o, dO, workspace})) return SWATTN_ERR_INVALID_ARG;
+  return hip_status(swattn::launch_bwd_pre(bf16, o, dO, (float *)workspace, B, H, T, D, st));
+}
+
+int bwd_dkdv(bool bf16, const void *q, const void *k, const void *v, const void *dO,
+             const float *lse, const void *workspace, void *dk, void *dv, int B, int H, int T,
+             int D, int window, float scale, hipStream_t st) {
+  int s = check_common(B, H, T, D, window);
+  if (s != SWATTN_OK) return s;
+  if (!all_aligned({q, k, v, dO, workspace, dk, dv}) || lse == nullptr)
+    return SWATTN_ERR_INVALID_ARG;
+  return hip_status(swattn::launch_bwd_dkdv(bf16, q, k, v, dO, lse, (const float *)workspace, dk,
+                                            dv, B, H, T, D, window, scale, st));
+}
+
+int bwd_dq(bool bf16, const void *q, const void *k, const void *v, const void *dO,
+           const float *lse, const void *workspace, void *dq, int B, int H, int T, int D,
+           int window, float scale, hipStream_t st) {
+  int s = check_common(B, H, T, D, window);
+  if (s != SWATTN_OK) return s;
+  if (!all_aligned({q, k, v, dO, workspace, dq}) || lse == nullptr) return SWATTN_ERR_INVALID_ARG;
+  return hip_status(swattn::launch_bwd_dq(bf16, q, k, v, dO, lse, (const float *)workspace, dq, B,
+                                          H, T, D, window, scale, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *swattn_status_string(int status) {
+  switch (status) {
+    case SWATTN_OK: return "SWATTN_OK";
+    case SWATTN_ERR_INVALID_ARG: return "SWATTN_ERR_INVALID_ARG";
+    case SWATTN_ERR_UNSUPPORTED: return "SWATTN_ERR_UNSUPPORTED";
+    case SWATTN_ERR_HIP: return "SWATTN_ERR_HIP";
+    default: return "SWATTN_ERR_UNKNOWN";
+  }
+}
+
+int swattn_version(void) { return kVersion; }
+
+int swattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+               int T, int D, int window, float scale, swattn_stream_t stream) {
+  int st = check_common(B, H, T, D, window);
+  if (st != SWATTN_OK) return st;
+  if (!all_aligned({q, k, v, o}) || lse == nullptr) return SWATTN_ERR_INVALID_ARG;
+  return hip_status(swattn::launch_fwd_bf16(q, k, v, o, lse, B, H, T, D, window, scale,
+                                            (hipStream_t)stream));
+}
+
+int swattn_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse, int B,
+                   int H, int T, int D, int window, float scale, swattn_stream_t stream) {
+  int st = check_common(B, H, T, D, window);
+  if (st != SWATTN_OK) return st;
+  if (!all_aligned({q, k, v, o}) || lse == nullptr) return SWATTN_ERR_INVALID_ARG;
+  return hip_status(swattn::launch_fwd_f32(q, k, v, o, lse, B, H, T, D, window, scale,
+                                           (hipStream_t)stream));
+}
+
+size_t swattn_bwd_workspace_size(int B, int H, int T, int D) {
+  if (check_common(B, H, T, D, -1) != SWATTN_OK) return 0;
+  const size_t bytes = (size_t)B * H * T * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int swattn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dO,
+               const float *lse, void *dq, void *dk, void *dv, int B, int H, int T, int D,
+               int window, float scale, void *workspace, swattn_stream_t stream) {
+  return bwd_all(true, q, k, v, o, dO, lse, dq, dk, dv, B, H, T, D, window, scale, workspace,
+                 (hipStream_t)stream);
+}
+
+int swattn_bwd_f32(const float *q, const float *k, const float *v, const float *o,
+                   const float *dO, const float *lse, float *dq, float *dk, float *dv, int B,
+                   int H, int T, int D, int window, float scale, void *workspace,
+                   swattn_stream_t stream) {
+  return bwd_all(false, q, k, v, o, dO, lse, dq, dk, dv, B, H, T, D, window, scale, workspace,
+                 (hipStream_t)stream);
+}
+
+int swattn_bwd_preprocess(const void *o, const void *dO, void *workspace, int B, int H, int T,
+                          int D, swattn_stream_t stream) {
+  return bwd_pre(true, o, dO, workspace, B, H, T, D, (hipStream_t)stream);
+}
+
+int swattn_bwd_preprocess_f32(const float *o, const float *dO, void *workspace, int B, int H,
+                              int T, int D, swattn_stream_t stream) {
+  return bwd_pre(false, o, dO, workspace, B, H, T, D, (hipStream_t)stream);
+}
+
+int swattn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dO, const float *lse,
+                    const void *workspace, void *dk, void *dv, int B, int H, int T, int D,
+                    int window, float scale, swattn_stream_t stream) {
+  return bwd_dkdv(true, q, k, v, dO, lse, workspace, dk, dv, B, H, T, D, window, scale,
+                  (hipStream_t)stream);
+}
+
+int swattn_bwd_dkdv_f32(const float *q, const float *k, const float *v, const float *dO,
+                        const float *lse, const void *workspace, float *dk, float *dv, int B,
+                        int H, int T, int D, int window, float scale, swattn_stream_t stream) {
+  return bwd_dkdv(false, q, k, v, dO, lse, workspace, dk, dv, B, H, T, D, window, scale,
+                  (hipStream_t)stream);
+}
+
+int swattn_bwd_dq(const void *q, const void *k, const void *v, const void *dO, const float *lse,
+                  const void *workspace, void *dq, int B, int H, int T, int D, int window,
+                  float scale, swattn_stream_t stream) {
+  return bwd_dq(true, q, k, v, dO, lse, workspace, dq, B, H, T, D, window, scale,
+                (hipStream_t)stream);
+}
+
+int swattn_bwd_dq_f32(const float *q, const float *k, const float *v, const float *dO,
+                      const float *lse, const void *workspace, float *dq, int B, int H, int T,
+                      int D, int window, float scale, swattn_stream_t stream) {
+  return bwd_dq(false, q, k, v, dO, lse, workspace, dq, B, H, T, D, window, scale,
+                (hipStream_t)stream);
+}
+
+size_t swattn_decode_workspace_size(int B, int H, int D, int Tmax, int window) {
+  if (check_decode(B, H, D, Tmax, window) != SWATTN_OK) return 0;
+  const size_t ns = (size_t)swattn::decode_num_splits(Tmax, window);
+  const size_t bytes = (size_t)B * H * ns * (D + 1) * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+static int decode_common(bool bf16, const void *q, const void *k_cache, const void *v_cache,
+                         const int *seqlens, void *o, float *lse, int B, int H, int D, int Tmax,
+                         int window, float scale, void *workspace, swattn_stream_t stream) {
+  int st = check_decode(B, H, D, Tmax, window);
+  if (st != SWATTN_OK) return st;
+  if (!all_aligned({q, k_cache, v_cache, o, workspace}) || seqlens == nullptr)
+    return SWATTN_ERR_INVALID_ARG;
+  return hip_status(swattn::launch_decode(bf16, q, k_cache, v_cache, seqlens, o, lse, B, H, D,
+                                          Tmax, window, scale, (float *)workspace,
+                                          (hipStream_t)stream));
+}
+
+int swattn_decode(const void *q, const void *k_cache, const void *v_cache, const int *seqlens,
+                  void *o, float *lse, int B, int H, int D, int Tmax, int window, float scale,
+                  void *workspace, swattn_stream_t stream) {
+  return decode_common(true, q, k_cache, v_cache, seqlens, o, lse, B, H, D, Tmax, window, scale,
+                       workspace, stream);
+}
+
+int swattn_decode_f32(const float *q, const float *k_cache, const float *v_cache,
+                      const int *seqlens, float *o, float *lse, int B, int H, int D, int Tmax,
+                      int window, float scale, void *workspace, swattn_stream_t stream) {
+  return decode_common(false, q, k_cache, v_cache, seqlens, o, lse, B, H, D, Tmax, window, scale,
+                       workspace, stream);
+}
+
+}  // extern "C"

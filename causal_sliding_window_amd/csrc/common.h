@@ -1,0 +1,118 @@
+// Shared device helpers for the libswattn kernels (gfx950 only).
+//
+// MFMA conventions (v_mfma_f32_32x32x16_bf16, wave64), checked on the hardware:
+//   A operand (32 x 16, M x K): lane l holds A[l % 32][8*(l/32) + j], j = 0..7
+//   B operand (16 x 32, K x N): lane l holds B[8*(l/32) + j][l % 32]
+//   C/D (32 x 32 fp32):         lane l, register i holds C[8*(i/4) + 4*(l/32) + i%4][l % 32]
+// LDS transpose read ds_read_b64_tr_b16, per 16-lane group: lane i = 4c + e
+// receives out[r] = (4 x b16 chunk addressed by lane 4r + c)[e], r = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// MFMA row m of a 32-row operand block maps to tile row swap23(m) (bits 2 and 3
+// exchanged).  With this order, the C registers 8t..8t+7 of a lane in half h
+// hold tile rows 16t + 8h + 0..7, which is exactly the B-operand (K = row) slot
+// order of the next MFMA: a C tile feeds the next product without data movement.
+__device__ __forceinline__ int swap23(int m) {
+  return (m & ~12) | ((m & 8) >> 1) | ((m & 4) << 1);
+}
+
+// Tile row held by C register i of a lane in half h (for a 32-row block).
+__device__ __forceinline__ int c_row(int i, int h) {
+  return swap23(8 * (i >> 2) + 4 * h + (i & 3));
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Max / sum of a value and the same register in the other 32-lane half.
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Eight fp32 -> bf16 (round to nearest even) as an MFMA operand.
+__device__ __forceinline__ bf16x8 to_bf16x8(f32x16 s, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (__bf16)s[base + j];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const uint16_t *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+// Transposed LDS read: 4 x bf16 (see the header comment for the lane mapping).
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4 *)(reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// A-operand (M = column of a row-major LDS tile, K = 8 consecutive tile rows) of a
+// 32 x 16 block read with two transposed reads.  `base` points at tile element
+// (row0, col0); rows row0 + 8h + 0..7 and columns col0 + (l % 32) are delivered
+// to lane l in the A-operand order.  `ld` is the tile row pitch in elements.
+// The same call also yields a B operand (K = rows, N = columns).
+__device__ __forceinline__ bf16x8 lds_read_tr_block(const uint16_t *base, int ld, int lane) {
+  const int h = lane >> 5;
+  const int g = (lane >> 4) & 1;
+  const int i = lane & 15;
+  const uint16_t *p = base + (8 * h + (i >> 2)) * ld + 16 * g + 4 * (i & 3);
+  return cat(lds_read_tr(p), lds_read_tr(p + 4 * ld));
+}
+
+// Same as lds_read_tr_block, for a tile whose 32-row blocks are stored in swap23
+// order (LDS row swap23(r) holds tile row r): rows 8h + 0..3 sit at LDS rows
+// 4h + 0..3 and rows 8h + 4..7 at LDS rows 8 + 4h + 0..3.
+__device__ __forceinline__ bf16x8 lds_read_tr_block_perm(const uint16_t *base, int ld, int lane) {
+  const int h = lane >> 5;
+  const int g = (lane >> 4) & 1;
+  const int i = lane & 15;
+  const uint16_t *p = base + (4 * h + (i >> 2)) * ld + 16 * g + 4 * (i & 3);
+  return cat(lds_read_tr(p), lds_read_tr(p + 8 * ld));
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+}  // namespace swattn

@@ -1,0 +1,51 @@
+// Internal launchers shared by the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace swattn {
+
+// Number of KV rows one decode workgroup handles.
+constexpr int kDecodeChunk = 256;
+
+int decode_num_splits(int Tmax, int window);
+
+hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int B, int H, int T, int D, int window, float scale, hipStream_t st);
+hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
+                          int B, int H, int T, int D, int window, float scale, hipStream_t st);
+
+// Backward passes; `bf16` selects the bf16 MFMA kernels, else the fp32 ones.
+hipError_t launch_bwd_pre(bool bf16, const void *o, const void *dO, float *delta, int B, int H,
+                          int T, int D, hipStream_t st);
+hipError_t launch_bwd_dkdv(bool bf16, const void *q, const void *k, const void *v,
+                           const void *dO, const float *lse, const float *delta, void *dk,
+                           void *dv, int B, int H, int T, int D, int window, float scale,
+                           hipStream_t st);
+hipError_t launch_bwd_dq(bool bf16, const void *q, const void *k, const void *v, const void *dO,
+                         const float *lse, const float *delta, void *dq, int B, int H, int T,
+                         int D, int window, float scale, hipStream_t st);
+
+hipError_t launch_bwd_pre_bf16(const void *o, const void *dO, float *delta, int B, int H, int T,
+                               int D, hipStream_t st);
+hipError_t launch_bwd_dkdv_bf16(const void *q, const void *k, const void *v, const void *dO,
+                                const float *lse, const float *delta, void *dk, void *dv, int B,
+                                int H, int T, int D, int window, float scale, hipStream_t st);
+hipError_t launch_bwd_dq_bf16(const void *q, const void *k, const void *v, const void *dO,
+                              const float *lse, const float *delta, void *dq, int B, int H,
+                              int T, int D, int window, float scale, hipStream_t st);
+hipError_t launch_bwd_pre_f32(const float *o, const float *dO, float *delta, int B, int H, int T,
+                              int D, hipStream_t st);
+hipError_t launch_bwd_dkdv_f32(const float *q, const float *k, const float *v, const float *dO,
+                               const float *lse, const float *delta, float *dk, float *dv, int B,
+                               int H, int T, int D, int window, float scale, hipStream_t st);
+hipError_t launch_bwd_dq_f32(const float *q, const float *k, const float *v, const float *dO,
+                             const float *lse, const float *delta, float *dq, int B, int H, int T,
+                             int D, int window, float scale, hipStream_t st);
+
+hipError_t launch_decode(bool bf16, const void *q, const void *k_cache, const void *v_cache,
+                         const int *seqlens, void *o, float *lse, int B, int H, int D, int Tmax,
+                         int window, float scale, float *ws, hipStream_t st);
+
+}  // namespace swattn

@@ -1,0 +1,259 @@
+"""Thin Python binding of libswattn (argument marshalling only).
+
+The entry points carry the C names of ``include/swattn.h`` and take torch tensors
+that live on the GPU; every step of the computation runs in the HIP kernels of
+``libswattn.so``.  Torch is used for device memory and streams only.  There is no
+fallback: if the library is missing or fails to load, every call raises.
+
+Convenience wrappers ``fwd``, ``bwd`` and ``decode`` allocate the outputs (and the
+workspace) with torch and call the matching entry point for the input dtype.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libswattn.so")
+
+SWATTN_OK = 0
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+_SIGS = {
+    "swattn_status_string": ([_I], ctypes.c_char_p),
+    "swattn_version": ([], _I),
+    "swattn_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P], _I),
+    "swattn_fwd_f32": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P], _I),
+    "swattn_bwd_workspace_size": ([_I, _I, _I, _I], ctypes.c_size_t),
+    "swattn_bwd": ([_P] * 9 + [_I] * 5 + [_F, _P, _P], _I),
+    "swattn_bwd_f32": ([_P] * 9 + [_I] * 5 + [_F, _P, _P], _I),
+    "swattn_bwd_preprocess": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "swattn_bwd_preprocess_f32": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "swattn_bwd_dkdv": ([_P] * 8 + [_I] * 5 + [_F, _P], _I),
+    "swattn_bwd_dkdv_f32": ([_P] * 8 + [_I] * 5 + [_F, _P], _I),
+    "swattn_bwd_dq": ([_P] * 7 + [_I] * 5 + [_F, _P], _I),
+    "swattn_bwd_dq_f32": ([_P] * 7 + [_I] * 5 + [_F, _P], _I),
+    "swattn_decode_workspace_size": ([_I] * 5, ctypes.c_size_t),
+    "swattn_decode": ([_P] * 6 + [_I] * 5 + [_F, _P, _P], _I),
+    "swattn_decode_f32": ([_P] * 6 + [_I] * 5 + [_F, _P, _P], _I),
+}
+
+
+class SwattnError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libswattn.so once (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise SwattnError(
+                f"{LIB_PATH} is missing: build it with `python -m causal_sliding_window_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = h
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().swattn_status_string(int(code)).decode()
+
+
+def _check(code: int, what: str):
+    if code != SWATTN_OK:
+        raise SwattnError(f"{what} failed: {status_string(code)}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_tensor(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise SwattnError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise SwattnError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise SwattnError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise SwattnError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _kind(dtype):
+    if dtype == torch.bfloat16:
+        return ""
+    if dtype == torch.float32:
+        return "_f32"
+    raise SwattnError(f"unsupported dtype {dtype}; use bfloat16 or float32")
+
+
+# ----------------------------------------------------------------------------- C-named entries
+def swattn_fwd(q, k, v, o, lse, window: int, scale: float, stream=None):
+    """Forward into preallocated o [B,T,H,D] and lse [B,H,T] (float32)."""
+    B, T, H, D = q.shape
+    suf = _kind(q.dtype)
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _dev_tensor(t, n, q.dtype, (B, T, H, D))
+    _dev_tensor(lse, "lse", torch.float32, (B, H, T))
+    fn = getattr(lib(), "swattn_fwd" + suf)
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, T, D, int(window),
+              float(scale), _stream(stream, q.device)), "swattn_fwd" + suf)
+
+
+swattn_fwd_f32 = swattn_fwd
+
+
+def swattn_bwd_workspace_size(B: int, H: int, T: int, D: int) -> int:
+    return int(lib().swattn_bwd_workspace_size(B, H, T, D))
+
+
+def swattn_bwd(q, k, v, o, do, lse, dq, dk, dv, window: int, scale: float, workspace,
+               stream=None):
+    """Backward into preallocated dq, dk, dv; ``workspace`` is a uint8 GPU tensor."""
+    B, T, H, D = q.shape
+    suf = _kind(q.dtype)
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk),
+                 ("dv", dv)):
+        _dev_tensor(t, n, q.dtype, (B, T, H, D))
+    _dev_tensor(lse, "lse", torch.float32, (B, H, T))
+    _dev_tensor(workspace, "workspace")
+    if workspace.numel() * workspace.element_size() < swattn_bwd_workspace_size(B, H, T, D):
+        raise SwattnError("workspace too small")
+    fn = getattr(lib(), "swattn_bwd" + suf)
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+              _ptr(dv), B, H, T, D, int(window), float(scale), _ptr(workspace),
+              _stream(stream, q.device)), "swattn_bwd" + suf)
+
+
+swattn_bwd_f32 = swattn_bwd
+
+
+def _bwd_stage_checks(q, tensors, lse, workspace):
+    B, T, H, D = q.shape
+    for n, t in tensors:
+        _dev_tensor(t, n, q.dtype, (B, T, H, D))
+    if lse is not None:
+        _dev_tensor(lse, "lse", torch.float32, (B, H, T))
+    _dev_tensor(workspace, "workspace")
+    if workspace.numel() * workspace.element_size() < swattn_bwd_workspace_size(B, H, T, D):
+        raise SwattnError("workspace too small")
+    return B, T, H, D
+
+
+def swattn_bwd_preprocess(o, do, workspace, stream=None):
+    """delta = rowsum(dO * o) into the workspace (first backward pass)."""
+    B, T, H, D = _bwd_stage_checks(o, (("o", o), ("do", do)), None, workspace)
+    fn = getattr(lib(), "swattn_bwd_preprocess" + _kind(o.dtype))
+    _check(fn(_ptr(o), _ptr(do), _ptr(workspace), B, H, T, D, _stream(stream, o.device)),
+           "swattn_bwd_preprocess")
+
+
+def swattn_bwd_dkdv(q, k, v, do, lse, workspace, dk, dv, window: int, scale: float, stream=None):
+    """dK, dV pass (needs the preprocess's workspace)."""
+    B, T, H, D = _bwd_stage_checks(q, (("q", q), ("k", k), ("v", v), ("do", do), ("dk", dk),
+                                       ("dv", dv)), lse, workspace)
+    fn = getattr(lib(), "swattn_bwd_dkdv" + _kind(q.dtype))
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(workspace), _ptr(dk), _ptr(dv),
+              B, H, T, D, int(window), float(scale), _stream(stream, q.device)), "swattn_bwd_dkdv")
+
+
+def swattn_bwd_dq(q, k, v, do, lse, workspace, dq, window: int, scale: float, stream=None):
+    """dQ pass (needs the preprocess's workspace)."""
+    B, T, H, D = _bwd_stage_checks(q, (("q", q), ("k", k), ("v", v), ("do", do), ("dq", dq)),
+                                   lse, workspace)
+    fn = getattr(lib(), "swattn_bwd_dq" + _kind(q.dtype))
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(workspace), _ptr(dq), B, H, T,
+              D, int(window), float(scale), _stream(stream, q.device)), "swattn_bwd_dq")
+
+
+swattn_bwd_preprocess_f32 = swattn_bwd_preprocess
+swattn_bwd_dkdv_f32 = swattn_bwd_dkdv
+swattn_bwd_dq_f32 = swattn_bwd_dq
+
+
+def swattn_decode_workspace_size(B: int, H: int, D: int, Tmax: int, window: int) -> int:
+    return int(lib().swattn_decode_workspace_size(B, H, D, Tmax, int(window)))
+
+
+def swattn_decode(q, k_cache, v_cache, seqlens, o, lse, window: int, scale: float, workspace,
+                  stream=None):
+    """Decode into preallocated o [B,H,D] (and lse [B,H] float32, or None)."""
+    B, H, D = q.shape
+    Tmax = k_cache.shape[1]
+    suf = _kind(q.dtype)
+    _dev_tensor(q, "q", q.dtype, (B, H, D))
+    _dev_tensor(o, "o", q.dtype, (B, H, D))
+    _dev_tensor(k_cache, "k_cache", q.dtype, (B, Tmax, H, D))
+    _dev_tensor(v_cache, "v_cache", q.dtype, (B, Tmax, H, D))
+    _dev_tensor(seqlens, "seqlens", torch.int32, (B,))
+    if lse is not None:
+        _dev_tensor(lse, "lse", torch.float32, (B, H))
+    _dev_tensor(workspace, "workspace")
+    if workspace.numel() * workspace.element_size() < swattn_decode_workspace_size(B, H, D, Tmax, window):
+        raise SwattnError("workspace too small")
+    fn = getattr(lib(), "swattn_decode" + suf)
+    _check(fn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse), B, H, D,
+              Tmax, int(window), float(scale), _ptr(workspace), _stream(stream, q.device)),
+           "swattn_decode" + suf)
+
+
+swattn_decode_f32 = swattn_decode
+
+
+# ----------------------------------------------------------------------------- allocating wrappers
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+def fwd(q, k, v, window: int = -1, scale: float | None = None, stream=None):
+    B, T, H, D = q.shape
+    scale = default_scale(D) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    swattn_fwd(q, k, v, o, lse, window, scale, stream)
+    return o, lse
+
+
+def bwd(q, k, v, o, do, lse, window: int = -1, scale: float | None = None, stream=None,
+        workspace=None):
+    B, T, H, D = q.shape
+    scale = default_scale(D) if scale is None else scale
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty(swattn_bwd_workspace_size(B, H, T, D), dtype=torch.uint8,
+                                device=q.device)
+    swattn_bwd(q, k, v, o, do, lse, dq, dk, dv, window, scale, workspace, stream)
+    return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, seqlens, window: int = -1, scale: float | None = None,
+           stream=None, workspace=None, with_lse: bool = True):
+    B, H, D = q.shape
+    Tmax = k_cache.shape[1]
+    scale = default_scale(D) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if with_lse else None
+    if workspace is None:
+        workspace = torch.empty(swattn_decode_workspace_size(B, H, D, Tmax, window),
+                                dtype=torch.uint8, device=q.device)
+    swattn_decode(q, k_cache, v_cache, seqlens, o, lse, window, scale, workspace, stream)
+    return o, lse

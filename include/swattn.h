@@ -1,0 +1,166 @@
+/*
+ * libswattn — causal multi-head attention with an optional sliding window,
+ * forward, backward and one-token KV-cache decode, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the nanochat pages):
+ *   - nanochat guide ("Train your own ChatGPT", apidog), section 5 "Flash Attention
+ *     unification": every attention layer makes one call with q, k, v, causal
+ *     masking switched on and a window_size argument; off Hopper the same call is
+ *     PyTorch's scaled-dot-product attention, i.e. plain masked softmax(scale*QK^T)V.
+ *   - same guide, section 1 "GPT model", feature list: sliding-window attention
+ *     whose window alternates between short and long across layers ("SSSL").
+ *   - time-to-GPT-2 post (Jan-29 leaderboard), list of the biggest wins: the FA3
+ *     kernels are faster and take the window_size argument.
+ *   - same guide, section 6 "Inference engine": the engine keeps a KV cache that
+ *     the kernels read (with-KV-cache entry) while decoding one token at a time.
+ *
+ * Definitions used by every entry point (positions are 0-based):
+ *   visible(i, j)  <=>  j <= i  and  (window < 0  or  i - j < window)
+ *   s_ij = scale * q_i . k_j;  LSE_i = ln sum_{visible j} exp(s_ij)   (natural log)
+ *   p_ij = exp(s_ij - LSE_i) on visible entries;  o_i = sum_j p_ij v_j
+ *   window = W >= 1: a query sees its W most recent keys, itself included
+ *   (FlashAttention's window_size = (W-1, 0)); window < 0: full causal;
+ *   window == 0 is an error; W >= T equals full causal.
+ *
+ * Layout and types.
+ *   - q, k, v, o, dO, dq, dk, dv: device memory, contiguous [B, T, H, D] (D fastest).
+ *     Plain names take bf16 (raw 16-bit storage); the _f32 names take float32.
+ *   - lse: device float32 [B, H, T].  Decode q/o: [B, H, D]; decode lse: [B, H].
+ *   - k_cache, v_cache: device, contiguous [B, Tmax, H, D].
+ *   - seqlens: device int32 [B].
+ *   - D must be 64 or 128.  All arithmetic accumulates in float32; bf16 outputs
+ *     are rounded to nearest even.
+ *
+ * Ownership and execution.
+ *   - The caller allocates every buffer (including workspaces) and keeps it alive
+ *     until the work on `stream` has finished.  The library allocates and frees
+ *     nothing, keeps no global state and is safe to call from several threads.
+ *   - Calls only enqueue kernels on `stream` (NULL = the default stream) and never
+ *     synchronise the host.  Pass a hipStream_t; it is declared here as an opaque
+ *     pointer so that this header needs no HIP include.
+ *   - Outputs must not alias inputs.
+ *
+ * Errors: every entry point returns a swattn_status; nothing is thrown.
+ *   SWATTN_ERR_INVALID_ARG  NULL required pointer, B/H/T/D/Tmax <= 0, window == 0,
+ *                           a size product that does not fit the kernels' 32-bit
+ *                           grid/row indices, or a workspace pointer of NULL
+ *   SWATTN_ERR_UNSUPPORTED  D not in {64, 128}
+ *   SWATTN_ERR_HIP          the HIP runtime reported an error at launch
+ * On an error nothing has been enqueued (argument errors) or the state of the
+ * outputs is unspecified (HIP errors).
+ */
+#ifndef SWATTN_H
+#define SWATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *swattn_stream_t; /* == hipStream_t */
+
+typedef enum {
+  SWATTN_OK = 0,
+  SWATTN_ERR_INVALID_ARG = 1,
+  SWATTN_ERR_UNSUPPORTED = 2,
+  SWATTN_ERR_HIP = 3
+} swattn_status;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *swattn_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int swattn_version(void);
+
+/*
+ * Forward: o = softmax(scale*QK^T, masked)V and lse (guide section 5; window from
+ * section 1).  Inputs q, k, v; outputs o (same dtype as q) and lse (float32,
+ * [B,H,T]).  Row i of o only depends on rows j <= i of k and v.
+ */
+int swattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+               int B, int H, int T, int D, int window, float scale,
+               swattn_stream_t stream);
+int swattn_fwd_f32(const float *q, const float *k, const float *v, float *o,
+                   float *lse, int B, int H, int T, int D, int window,
+                   float scale, swattn_stream_t stream);
+
+/*
+ * Backward workspace in bytes: delta_i = dO_i . o_i, float32 [B,H,T], rounded up
+ * to 256 bytes.  Returns 0 for invalid sizes.
+ */
+size_t swattn_bwd_workspace_size(int B, int H, int T, int D);
+
+/*
+ * Backward: gradients of L = sum_i dO_i . o_i with respect to q, k, v, given the
+ * forward's o and lse (the analytic gradient of the guide's section-5 attention;
+ * training back-propagates through it).  P is recomputed from lse; dK/dV and dQ
+ * are produced by separate passes with no atomics, so results are bitwise
+ * reproducible.  dq, dk, dv have q's dtype.  `workspace` must hold
+ * swattn_bwd_workspace_size() bytes; its contents on entry do not matter.
+ */
+int swattn_bwd(const void *q, const void *k, const void *v, const void *o,
+               const void *dO, const float *lse, void *dq, void *dk, void *dv,
+               int B, int H, int T, int D, int window, float scale,
+               void *workspace, swattn_stream_t stream);
+int swattn_bwd_f32(const float *q, const float *k, const float *v,
+                   const float *o, const float *dO, const float *lse, float *dq,
+                   float *dk, float *dv, int B, int H, int T, int D, int window,
+                   float scale, void *workspace, swattn_stream_t stream);
+
+/*
+ * The three passes of swattn_bwd, callable on their own (to time them, or to run
+ * the two independent gradient passes on different streams).  swattn_bwd is
+ * exactly: swattn_bwd_preprocess (delta = rowsum(dO * o) into the workspace), then
+ * swattn_bwd_dkdv and swattn_bwd_dq, which both read that workspace and may run in
+ * either order or concurrently once the preprocess has finished.
+ */
+int swattn_bwd_preprocess(const void *o, const void *dO, void *workspace, int B, int H,
+                          int T, int D, swattn_stream_t stream);
+int swattn_bwd_preprocess_f32(const float *o, const float *dO, void *workspace, int B,
+                              int H, int T, int D, swattn_stream_t stream);
+int swattn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dO,
+                    const float *lse, const void *workspace, void *dk, void *dv, int B,
+                    int H, int T, int D, int window, float scale,
+                    swattn_stream_t stream);
+int swattn_bwd_dkdv_f32(const float *q, const float *k, const float *v,
+                        const float *dO, const float *lse, const void *workspace,
+                        float *dk, float *dv, int B, int H, int T, int D, int window,
+                        float scale, swattn_stream_t stream);
+int swattn_bwd_dq(const void *q, const void *k, const void *v, const void *dO,
+                  const float *lse, const void *workspace, void *dq, int B, int H, int T,
+                  int D, int window, float scale, swattn_stream_t stream);
+int swattn_bwd_dq_f32(const float *q, const float *k, const float *v, const float *dO,
+                      const float *lse, const void *workspace, float *dq, int B, int H,
+                      int T, int D, int window, float scale, swattn_stream_t stream);
+
+/*
+ * Decode workspace in bytes: per (sequence, head, KV split) one float32 partial
+ * output [D] and one partial LSE.  Depends on Tmax and window because they bound
+ * the number of splits.  Returns 0 for invalid sizes.
+ */
+size_t swattn_decode_workspace_size(int B, int H, int D, int Tmax, int window);
+
+/*
+ * One-token decode against a KV cache (guide section 6).  Sequence b has
+ * L = seqlens[b] valid cache rows, the new token's own K/V already written at row
+ * L-1; its query sits at position L-1 and sees rows max(0, L-W) .. L-1 (all rows
+ * 0 .. L-1 when window < 0).  Rows >= L are never read.  seqlens is read on the
+ * device; values above Tmax are clamped to Tmax, and L <= 0 yields o = 0 and
+ * lse = -inf.  lse may be NULL.  The visible range is split across workgroups
+ * and the partial results are merged by their LSE.
+ */
+int swattn_decode(const void *q, const void *k_cache, const void *v_cache,
+                  const int *seqlens, void *o, float *lse, int B, int H, int D,
+                  int Tmax, int window, float scale, void *workspace,
+                  swattn_stream_t stream);
+int swattn_decode_f32(const float *q, const float *k_cache,
+                      const float *v_cache, const int *seqlens, float *o,
+                      float *lse, int B, int H, int D, int Tmax, int window,
+                      float scale, void *workspace, swattn_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWATTN_H */

@@ -103,20 +103,24 @@ def head_fwd(q, k, v, window: int, scale: float):
     return o, lse
 
 
-def head_bwd(q, k, v, do, window: int, scale: float):
+def head_bwd(q, k, v, do, window: int, scale: float, o=None):
     """Analytic gradients of ``L = sum_i dO_i . o_i`` for one head.
 
     With p from :func:`head_probs` and o = p v:
       dv = p^T dO;  dp = dO v^T;  delta_i = dO_i . o_i;
       ds = p * (dp - delta);  dq = scale * ds k;  dk = scale * ds^T q.
     Returns (dq, dk, dv), each [T, D].
+
+    ``o``: optional forward output to take delta from (the backward entry point
+    receives the stored forward output and forms delta from it); by default the
+    exact o = p v is used, which gives the exact gradient.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     p, _ = head_probs(q, k, window, scale)
-    o = p @ v
+    o = p @ v if o is None else np.asarray(o, dtype=np.float64)
     dv = p.T @ do
     dp = do @ v.T
     delta = (do * o).sum(axis=1)
@@ -148,8 +152,9 @@ def attn_fwd(q, k, v, window: int, scale: float, heads=None):
     return o, lse
 
 
-def attn_bwd(q, k, v, do, window: int, scale: float, heads=None):
-    """Backward over [B, T, H, D] arrays -> (dq, dk, dv); see :func:`head_bwd`."""
+def attn_bwd(q, k, v, do, window: int, scale: float, heads=None, o=None):
+    """Backward over [B, T, H, D] arrays -> (dq, dk, dv); see :func:`head_bwd`
+    (``o``, optional [B, T, H, D]: the forward output delta is taken from)."""
     q = np.asarray(q, dtype=np.float64)
     B, T, H, D = q.shape
     dq = np.full((B, T, H, D), np.nan)
@@ -158,7 +163,7 @@ def attn_bwd(q, k, v, do, window: int, scale: float, heads=None):
     for b, h in _heads(B, H, heads):
         dq[b, :, h, :], dk[b, :, h, :], dv[b, :, h, :] = head_bwd(
             q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], do[b, :, h, :],
-            window, scale)
+            window, scale, None if o is None else o[b, :, h, :])
     return dq, dk, dv
 
 

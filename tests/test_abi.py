@@ -1,0 +1,100 @@
+"""The C ABI library: it loads, exports every declared symbol, shares torch's HIP
+runtime, and rejects bad arguments before launching anything (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (load torch's HIP runtime first, as the binding does)
+
+from causal_sliding_window_amd import swattn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swattn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("swattn_fwd", "swattn_bwd", "swattn_decode", "swattn_fwd_f32", "swattn_bwd_f32",
+              "swattn_decode_f32", "swattn_bwd_workspace_size", "swattn_decode_workspace_size",
+              "swattn_status_string", "swattn_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = swattn.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_single_hip_runtime_in_process():
+    swattn.lib()
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) <= 1, paths
+
+
+def test_status_strings_and_version():
+    assert swattn.status_string(0) == "SWATTN_OK"
+    assert swattn.status_string(1) == "SWATTN_ERR_INVALID_ARG"
+    assert swattn.status_string(2) == "SWATTN_ERR_UNSUPPORTED"
+    assert swattn.status_string(3) == "SWATTN_ERR_HIP"
+    assert swattn.status_string(99) == "SWATTN_ERR_UNKNOWN"
+    assert swattn.lib().swattn_version() >= 100
+
+
+def test_workspace_sizes():
+    assert swattn.swattn_bwd_workspace_size(8, 6, 2048, 128) == 8 * 6 * 2048 * 4
+    assert swattn.swattn_bwd_workspace_size(1, 1, 3, 64) == 256
+    assert swattn.swattn_bwd_workspace_size(1, 1, 3, 96) == 0
+    assert swattn.swattn_bwd_workspace_size(0, 1, 3, 64) == 0
+    # 4096 rows in chunks of 256 -> 16 splits; a 1024 window -> 4
+    assert swattn.swattn_decode_workspace_size(32, 12, 128, 4096, -1) == 32 * 12 * 16 * 129 * 4
+    assert swattn.swattn_decode_workspace_size(32, 12, 128, 4096, 1024) == 32 * 12 * 4 * 129 * 4
+    assert swattn.swattn_decode_workspace_size(1, 1, 128, 4096, 0) == 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced (arguments fail first)
+MISALIGNED = ctypes.c_void_p((1 << 20) + 2)
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 64, 0, 1.0, None), 1),        # window == 0
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 8, 64, -1, 1.0, None), 1),       # B == 0
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, -3, 64, -1, 1.0, None), 1),      # T < 0
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 96, -1, 1.0, None), 2),       # D unsupported
+    ((None, FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 64, -1, 1.0, None), 1),       # NULL q
+    ((FAKE, FAKE, FAKE, FAKE, None, 1, 1, 8, 64, -1, 1.0, None), 1),       # NULL lse
+    ((FAKE, MISALIGNED, FAKE, FAKE, FAKE, 1, 1, 8, 64, -1, 1.0, None), 1),  # misaligned k
+])
+def test_fwd_argument_errors(args, expect):
+    lib = swattn.lib()
+    assert lib.swattn_fwd(*args) == expect
+    assert lib.swattn_fwd_f32(*args) == expect
+
+
+def test_bwd_and_decode_argument_errors():
+    lib = swattn.lib()
+    p9 = [FAKE] * 9
+    assert lib.swattn_bwd(*p9, 1, 1, 8, 64, 0, 1.0, FAKE, None) == 1
+    assert lib.swattn_bwd(*p9, 1, 1, 8, 64, -1, 1.0, None, None) == 1     # NULL workspace
+    assert lib.swattn_bwd_f32(*p9, 1, 1, 8, 32, -1, 1.0, FAKE, None) == 2
+    p6 = [FAKE] * 6
+    assert lib.swattn_decode(*p6, 1, 1, 128, 0, -1, 1.0, FAKE, None) == 1  # Tmax == 0
+    assert lib.swattn_decode(*p6, 1, 1, 128, 16, 0, 1.0, FAKE, None) == 1  # window == 0
+    assert lib.swattn_decode(*p6, 1, 1, 80, 16, -1, 1.0, FAKE, None) == 2
+    p6n = [FAKE, FAKE, FAKE, None, FAKE, FAKE]                               # NULL seqlens
+    assert lib.swattn_decode_f32(*p6n, 1, 1, 128, 16, -1, 1.0, FAKE, None) == 1
+
+
+def test_binding_rejects_host_tensors():
+    q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(swattn.SwattnError):
+        swattn.fwd(q, q, q)

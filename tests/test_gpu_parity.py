@@ -1,0 +1,274 @@
+"""GPU parity: libswattn (through the C ABI) against the fp64 oracle, same seeded inputs.
+
+Bars: float32 max-abs <= 1e-5 on o, lse, dq, dk, dv; bf16 max-abs <= 2e-2 and
+relative L2 <= 5e-3 on o, dq, dk, dv, and max-abs <= 1e-3 on lse.  The oracle is fed
+the exact rounded inputs upcast to float64.  Full-size workloads run exactly as the
+benchmark launches them and are compared on sampled heads (each head is independent).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from causal_sliding_window_amd import inputs, swattn
+from oracle import attention as orc
+from parity import check, f64, only_heads
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _gpu(x):
+    return {n: t.to(DEV) for n, t in x.items()}
+
+
+def run_fwd_bwd(g, window, scale):
+    o, lse = swattn.fwd(g["q"], g["k"], g["v"], window, scale)
+    dq, dk, dv = swattn.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, window, scale)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+def oracle_fwd_bwd(x, window, scale, heads=None):
+    a = {n: inputs.to_f64(t) for n, t in x.items()}
+    o, lse = orc.attn_fwd(a["q"], a["k"], a["v"], window, scale, heads)
+    dq, dk, dv = orc.attn_bwd(a["q"], a["k"], a["v"], a["do"], window, scale, heads)
+    return o, lse, dq, dk, dv
+
+
+def run_entry_points(x, window, scale):
+    """Forward vs oracle, and the backward entry point fed the oracle's own forward
+    output (rounded to the input dtype) and LSE, against the oracle's gradient with
+    delta taken from that same output.  Isolates each kernel from the other's rounding."""
+    a = {n: inputs.to_f64(t) for n, t in x.items()}
+    g = _gpu(x)
+    o, lse = swattn.fwd(g["q"], g["k"], g["v"], window, scale)
+    ro, rl = orc.attn_fwd(a["q"], a["k"], a["v"], window, scale)
+    o_in = torch.from_numpy(ro).to(x["q"].dtype)
+    lse_in = torch.from_numpy(rl).to(torch.float32)
+    dq, dk, dv = swattn.bwd(g["q"], g["k"], g["v"], o_in.to(DEV), g["do"], lse_in.to(DEV),
+                            window, scale)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = orc.attn_bwd(a["q"], a["k"], a["v"], a["do"], window, scale,
+                                 o=inputs.to_f64(o_in))
+    return (o, lse, dq, dk, dv), (ro, rl, rdq, rdk, rdv)
+
+
+def compare_all(got, ref, dtype, heads=None, tag=""):
+    names = ("o", "lse", "dq", "dk", "dv")
+    for n, g, r in zip(names, got, ref):
+        ga = f64(g)
+        if heads is not None:
+            ga = only_heads(ga, heads, "bht" if n == "lse" else "bthd")
+        check(f"{tag}{n}", ga, r, dtype, lse=(n == "lse"))
+
+
+# ----------------------------------------------------------------------------- fp32
+def test_tiny_config_fp32():
+    """B1 H2 T128 D64, fp32, full causal, seed 0: every output against the oracle."""
+    x = inputs.config_inputs("tiny")
+    scale = 1 / math.sqrt(64)
+    compare_all(run_fwd_bwd(_gpu(x), -1, scale), oracle_fwd_bwd(x, -1, scale), torch.float32)
+
+
+@pytest.mark.parametrize("T", [1, 33, 130, 257])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("W", [-1, 1, 17, 64])
+def test_fp32_shapes(T, D, W):
+    x = inputs.training_inputs(2, T, 2, D, "f32", seed=T + D + W)
+    scale = 1 / math.sqrt(D)
+    compare_all(run_fwd_bwd(_gpu(x), W, scale), oracle_fwd_bwd(x, W, scale), torch.float32)
+    compare_all(*run_entry_points(x, W, scale), torch.float32)
+
+
+# ----------------------------------------------------------------------------- bf16, small shapes
+@pytest.mark.parametrize("T", [1, 2, 63, 129, 300, 520])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("W", [-1, 1, 63, 65, 129, 256])
+def test_bf16_shapes(T, D, W):
+    """Ragged lengths and window edges mid-tile, inputs drawn like the training workloads."""
+    x = inputs.training_inputs(2, T, 3, D, "bf16", seed=7 * T + W, qk_norm=True)
+    scale = 1 / math.sqrt(D)
+    compare_all(*run_entry_points(x, W, scale), torch.bfloat16)
+
+
+def test_bf16_raw_normal_qk():
+    """Un-normalised N(0,1) Q and K: larger logits than the QK-normed workloads."""
+    x = inputs.training_inputs(2, 700, 2, 128, "bf16", seed=11, qk_norm=False)
+    scale = 1 / math.sqrt(128)
+    for W in (-1, 512):
+        compare_all(*run_entry_points(x, W, scale), torch.bfloat16)
+
+
+def test_long_sequence_sampled():
+    """T = 8192, one head, full causal and a 512 window (largest shape tested)."""
+    x = inputs.training_inputs(1, 8192, 1, 128, "bf16", seed=3, qk_norm=True)
+    scale = 1 / math.sqrt(128)
+    g = _gpu(x)
+    for W in (-1, 512):
+        compare_all(run_fwd_bwd(g, W, scale), oracle_fwd_bwd(x, W, scale), torch.bfloat16)
+
+
+# ----------------------------------------------------------------------------- full workloads
+@pytest.mark.parametrize("name", ["small", "wide-sw"])
+def test_full_config_all_heads(name):
+    """The workload exactly as benchmarked: GPU forward then GPU backward, every head
+    against the oracle's exact gradient."""
+    c = inputs.CONFIGS[name]
+    x = inputs.config_inputs(name)
+    scale = 1 / math.sqrt(c["D"])
+    W = c["windows"][0]
+    got = run_fwd_bwd(_gpu(x), W, scale)
+    compare_all(got, oracle_fwd_bwd(x, W, scale), torch.bfloat16, None, f"{name} ")
+
+
+def test_mid_alt_layer_schedule_all_heads():
+    """Four layers, windows 512/2048/512/2048: forwards 0..3 then backwards 3..0 on one stream."""
+    c = inputs.CONFIGS["mid-alt"]
+    scale = 1 / math.sqrt(c["D"])
+    xs = [inputs.config_inputs("mid-alt", layer) for layer in range(4)]
+    gs = [_gpu(x) for x in xs]
+    fw = [swattn.fwd(g["q"], g["k"], g["v"], W, scale) for g, W in zip(gs, c["windows"])]
+    bw = [None] * 4
+    for layer in (3, 2, 1, 0):
+        g, (o, lse) = gs[layer], fw[layer]
+        bw[layer] = swattn.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, c["windows"][layer], scale)
+    torch.cuda.synchronize()
+    for layer in range(4):
+        ref = oracle_fwd_bwd(xs[layer], c["windows"][layer], scale)
+        compare_all(fw[layer] + bw[layer], ref, torch.bfloat16, None, f"layer{layer} ")
+
+
+# ----------------------------------------------------------------------------- decode
+def _decode_oracle(d, W, scale):
+    a = {n: inputs.to_f64(d[n]) for n in ("q", "k_cache", "v_cache")}
+    return orc.attn_decode(a["q"], a["k_cache"], a["v_cache"], d["seqlens"].numpy(), W, scale)
+
+
+@pytest.mark.parametrize("W", [-1, 1024])
+def test_decode_config(W):
+    """32 sequences, H12 D128 bf16, lengths 512..4096 (seed 7): every sequence and head."""
+    d = inputs.config_inputs("decode")
+    g = _gpu(d)
+    scale = 1 / math.sqrt(128)
+    o, lse = swattn.decode(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], W, scale)
+    torch.cuda.synchronize()
+    ro, rl = _decode_oracle(d, W, scale)
+    check("decode o", o, ro, torch.bfloat16)
+    check("decode lse", lse, rl, torch.bfloat16, lse=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("W", [-1, 1, 100, 300])
+def test_decode_shapes(dtype, D, W):
+    lens = [1, 2, 255, 256, 257, 511, 700, 700]
+    d = inputs.decode_inputs(len(lens), 3, D, 700, dtype, seed=D + W, lengths=lens)
+    g = _gpu(d)
+    scale = 1 / math.sqrt(D)
+    o, lse = swattn.decode(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], W, scale)
+    torch.cuda.synchronize()
+    ro, rl = _decode_oracle(d, W, scale)
+    td = inputs.DTYPES[dtype]
+    check("o", o, ro, td)
+    check("lse", lse, rl, td, lse=True)
+
+
+def test_decode_clamps_and_empty():
+    """seqlens above Tmax is clamped to Tmax; seqlens 0 gives o = 0, lse = -inf."""
+    d = inputs.decode_inputs(3, 2, 128, 300, "bf16", seed=1, lengths=[0, 300, 300])
+    g = _gpu(d)
+    for n in ("q", "k_cache", "v_cache"):
+        g[n][2] = g[n][1]  # sequences 1 and 2 hold the same data
+    g["seqlens"] = torch.tensor([0, 5000, 300], dtype=torch.int32, device=DEV)
+    o, lse = swattn.decode(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], -1, 0.1)
+    torch.cuda.synchronize()
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.equal(o[1], o[2]) and torch.equal(lse[1], lse[2])
+
+
+def test_decode_never_reads_past_length():
+    lens = [5, 300, 1000]
+    d = inputs.decode_inputs(3, 4, 128, 1024, "bf16", seed=2, lengths=lens)
+    g = _gpu(d)
+    o1, l1 = swattn.decode(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], -1, 0.09)
+    for b, L in enumerate(lens):
+        g["k_cache"][b, L:] = float("nan")
+        g["v_cache"][b, L:] = float("nan")
+    o2, l2 = swattn.decode(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], -1, 0.09)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o2.float()).all()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_invariant_to_cache_padding():
+    d = inputs.decode_inputs(2, 2, 128, 600, "bf16", seed=4, lengths=[600, 333])
+    g = _gpu(d)
+    o1, l1 = swattn.decode(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], 256, 0.1)
+    big_k = torch.zeros(2, 2000, 2, 128, dtype=torch.bfloat16, device=DEV)
+    big_v = torch.zeros_like(big_k)
+    big_k[:, :600], big_v[:, :600] = g["k_cache"], g["v_cache"]
+    o2, l2 = swattn.decode(g["q"], big_k.contiguous(), big_v.contiguous(), g["seqlens"], 256, 0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("W", [-1, 200])
+def test_decode_matches_forward_last_row(W):
+    """Decode of the token at position L-1 equals forward row L-1 on the same prefix."""
+    T, H, D = 777, 4, 128
+    x = inputs.training_inputs(1, T, H, D, "bf16", seed=9, qk_norm=True)
+    g = _gpu(x)
+    o, lse = swattn.fwd(g["q"], g["k"], g["v"], W, 1 / math.sqrt(D))
+    q_last = g["q"][:, T - 1].contiguous()
+    od, ld = swattn.decode(q_last, g["k"], g["v"], torch.tensor([T], dtype=torch.int32, device=DEV),
+                           W, 1 / math.sqrt(D))
+    torch.cuda.synchronize()
+    assert (od.float() - o[:, T - 1].float()).abs().max().item() <= 2e-2
+    assert (ld - lse[:, :, T - 1]).abs().max().item() <= 1e-4
+
+
+# ----------------------------------------------------------------------------- properties
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_window_ge_T_bitwise_equals_full_causal(dtype):
+    T = 300
+    x = inputs.training_inputs(2, T, 2, 128, dtype, seed=1, qk_norm=True)
+    g = _gpu(x)
+    full = run_fwd_bwd(g, -1, 0.1)
+    for W in (T, T + 5, 1 << 20):
+        for a, b in zip(run_fwd_bwd(g, W, 0.1), full):
+            assert torch.equal(a, b)
+
+
+def test_repeat_calls_bitwise_deterministic():
+    x = inputs.training_inputs(2, 1000, 3, 128, "bf16", seed=8, qk_norm=True)
+    g = _gpu(x)
+    r1 = run_fwd_bwd(g, 333, 0.09)
+    r2 = run_fwd_bwd(g, 333, 0.09)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+def test_runs_on_a_side_stream():
+    x = inputs.training_inputs(1, 200, 2, 64, "bf16", seed=2, qk_norm=True)
+    g = _gpu(x)
+    ref = run_fwd_bwd(g, 50, 0.125)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = swattn.fwd(g["q"], g["k"], g["v"], 50, 0.125)
+        grads = swattn.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, 50, 0.125)
+    s.synchronize()
+    for a, b in zip((o, lse) + grads, ref):
+        assert torch.equal(a, b)
+
+
+def test_w1_gradients_vanish():
+    """W = 1: o = v and dv = dO after bf16 rounding; dq and dk vanish."""
+    x = inputs.training_inputs(1, 130, 2, 128, "bf16", seed=5, qk_norm=True)
+    o, lse, dq, dk, dv = run_fwd_bwd(_gpu(x), 1, 0.1)
+    assert torch.equal(o.cpu(), x["v"])
+    assert torch.equal(dv.cpu(), x["do"])
+    # dS = P (dP - delta) vanishes up to fp32 rounding (dP and delta are summed in different orders)
+    assert dq.abs().max().item() <= 1e-4 and dk.abs().max().item() <= 1e-4

@@ -180,8 +180,8 @@ def test_last_row_is_textbook_softmax():
 
 
 # ----------------------------------------------------------------------------- brute force
-def _brute(q, k, v, do, W, scale):
-    """Pure-Python loops, straight from the scalar definition."""
+def _brute(q, k, v, do, W, scale, o_given=None):
+    """Pure-Python loops, straight from the scalar definition (delta from o_given if set)."""
     T, D = len(q), len(q[0])
     vis = [[j <= i and (W < 0 or i - j < W) for j in range(T)] for i in range(T)]
     s = [[scale * sum(q[i][d] * k[j][d] for d in range(D)) for j in range(T)] for i in range(T)]
@@ -196,7 +196,8 @@ def _brute(q, k, v, do, W, scale):
                 p[i][j] = math.exp(s[i][j] - lse[i])
     o = [[sum(p[i][j] * v[j][d] for j in range(T)) for d in range(D)] for i in range(T)]
     dv = [[sum(p[i][j] * do[i][d] for i in range(T)) for d in range(D)] for j in range(T)]
-    delta = [sum(do[i][d] * o[i][d] for d in range(D)) for i in range(T)]
+    ob = o if o_given is None else o_given
+    delta = [sum(do[i][d] * ob[i][d] for d in range(D)) for i in range(T)]
     ds = [[p[i][j] * (sum(do[i][d] * v[j][d] for d in range(D)) - delta[i]) for j in range(T)]
           for i in range(T)]
     dq = [[scale * sum(ds[i][j] * k[j][d] for j in range(T)) for d in range(D)] for i in range(T)]
@@ -342,3 +343,19 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     p, _ = orc.head_probs(q, k, 2, 0.6)
     ds = p * (do @ v.T - (do * (p @ v)).sum(1)[:, None])
     assert not np.allclose(0.6 * (ds @ q), np.array(ref[3]))
+
+
+@pytest.mark.parametrize("T,W,D", [(5, -1, 3), (7, 3, 4)])
+def test_delta_from_given_output(T, W, D):
+    """With a supplied (perturbed) forward output, delta is taken from it; with the exact
+    output the result is the exact gradient."""
+    q, k, v, do = _rand(T, D), _rand(T, D), _rand(T, D), _rand(T, D)
+    o, _ = orc.head_fwd(q, k, v, W, 0.6)
+    for a, b in zip(orc.head_bwd(q, k, v, do, W, 0.6, o=o), orc.head_bwd(q, k, v, do, W, 0.6)):
+        np.testing.assert_allclose(a, b, atol=1e-14)
+    o_pert = o + 1e-3 * _rand(T, D)
+    ref = _brute(q.tolist(), k.tolist(), v.tolist(), do.tolist(), W, 0.6, o_pert.tolist())
+    got = orc.head_bwd(q, k, v, do, W, 0.6, o=o_pert)
+    for a, b in zip(got, ref[2:]):
+        np.testing.assert_allclose(a, np.array(b), atol=1e-12)
+    assert not np.allclose(got[0], orc.head_bwd(q, k, v, do, W, 0.6)[0], atol=1e-9)
