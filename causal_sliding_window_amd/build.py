@@ -26,6 +26,9 @@ HIPCC_FLAGS = [
     "-shared",
     # no packed-fp32 instructions anywhere (they are avoided on this hardware)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA results in arch VGPRs where they feed VALU work: avoids the
+    # accumulator <-> VGPR copies the default form generates
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -16,6 +16,8 @@
 // transposed LDS reads.  Inside the dQ pass S^T = K Q^T is formed with one query
 // per lane (as in the forward) and dS^T feeds dQ^T = K^T dS^T; K^T comes from
 // transposed LDS reads.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -53,12 +55,10 @@ template <int D>
 struct DkdvCfg {
   static constexpr int BK = 128;          // keys per workgroup (4 waves x 32)
   static constexpr int BQ = 64;           // queries per LDS tile
-  static constexpr int NT = 256;
-  static constexpr int QLD = D + 8;       // Q / dO tile pitch (elements)
-  static constexpr int QSZ = BQ * QLD;
-  static constexpr int CPR = D / 8;
-  static constexpr int RPP = NT / CPR;
-  static constexpr int PASSES = BQ / RPP;
+  static constexpr int TSZ = BQ * D;      // elements of one Q (or dO) tile
+  static constexpr int NDB = D / 32;
+  static constexpr int KST = D / 16;
+  static constexpr int CPW = (2 * TSZ * 2 / 1024) / 4;  // 1 KB copies per wave and tile
 };
 
 template <int D>
@@ -68,10 +68,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     const float *__restrict__ lse, const float *__restrict__ delta, uint16_t *__restrict__ dk,
     uint16_t *__restrict__ dv, int B, int H, int T, int window, float scale, int nkt) {
   using C = DkdvCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2 * C::QSZ];
-  __shared__ __attribute__((aligned(16))) uint16_t Gs[2 * C::QSZ];  // dO
-  __shared__ __attribute__((aligned(16))) float Ls[2 * C::BQ];        // lse * log2(e)
-  __shared__ __attribute__((aligned(16))) float Ds[2 * C::BQ];        // delta
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * C::TSZ];  // [buf][Q, dO]
+  __shared__ __attribute__((aligned(16))) float Ls[2 * C::BQ];             // lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float Ds[2 * C::BQ];             // delta
 
   const int BH = B * H;
   const int bid = blockIdx.x;
@@ -79,7 +78,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   const int bh = bid % BH;
   const int b = bh / H, hh = bh % H;
   const int k0 = kt * C::BK;
-  const size_t rs = (size_t)H * D;
+  const int rs = H * D;
   const size_t base = ((size_t)b * T * H + hh) * D;
   const uint16_t *qb = q + base, *kb = k + base, *vb = v + base, *gb = dO + base;
   const float *lseb = lse + (size_t)bh * T, *delb = delta + (size_t)bh * T;
@@ -94,138 +93,160 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   const int qt0 = k0 / C::BQ, qt1 = q_hi / C::BQ;
   const int wk_hi = min(T - 1, kw0 + 31);
   const int wq_hi = window > 0 ? wk_hi + window - 1 : T - 1;
+  // query qq sees key my_k iff 0 <= qq - my_k <= wm1
+  const unsigned wm1 = window > 0 ? (unsigned)(window - 1) : 0x7fffffffu;
 
-  bf16x8 kr[D / 16], vr[D / 16];
+  bf16x8 kr[C::KST], vr[C::KST];
+  {
+    const int row = min(my_k, T - 1);
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) {
-    if (my_k < T) {
-      kr[st] = *reinterpret_cast<const bf16x8 *>(kb + my_k * rs + 16 * st + 8 * h);
-      vr[st] = *reinterpret_cast<const bf16x8 *>(vb + my_k * rs + 16 * st + 8 * h);
-    } else {
-      kr[st] = bf16x8{};
-      vr[st] = bf16x8{};
+    for (int st = 0; st < C::KST; ++st) {
+      kr[st] = *reinterpret_cast<const bf16x8 *>(kb + (size_t)row * rs + 16 * st + 8 * h);
+      vr[st] = *reinterpret_cast<const bf16x8 *>(vb + (size_t)row * rs + 16 * st + 8 * h);
     }
   }
-  f32x16 dka[D / 32], dva[D / 32];
+  f32x16 dka[C::NDB], dva[C::NDB];
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d) {
+  for (int d = 0; d < C::NDB; ++d) {
     dka[d] = f32x16{};
     dva[d] = f32x16{};
   }
   const float c = scale * kLog2e;
 
-  u32x4 qreg[C::PASSES], greg[C::PASSES];
-  float lreg = 0.f, dreg = 0.f;
-  const int lrow = tid / C::CPR, lch = tid % C::CPR;
-
-  auto gload = [&](int qt) {
+  // Q and dO tiles: direct global -> LDS copies (rows in swap23 order).
+  auto issue_tile = [&](int qt, int buf) {
 #pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) {
-      const int qq = qt * C::BQ + lrow + p * C::RPP;
-      if (qq < T) {
-        qreg[p] = ldg16(qb + qq * rs + lch * 8);
-        greg[p] = ldg16(gb + qq * rs + lch * 8);
-      } else {
-        qreg[p] = u32x4{};
-        greg[p] = u32x4{};
-      }
-    }
-    if (tid < C::BQ) {
-      const int qq = qt * C::BQ + tid;
-      lreg = qq < T ? lseb[qq] * kLog2e : INFINITY;  // rows past T get p = 0
-      dreg = qq < T ? delb[qq] : 0.f;
+    for (int cc = 0; cc < C::CPW; ++cc) {
+      const int j = w * C::CPW + cc;
+      const int tensor = j / (4 * C::NDB), jj = j % (4 * C::NDB);
+      copy_rows16<C::BQ>(smem + (2 * buf + tensor) * C::TSZ, tensor ? gb : qb, rs, qt * C::BQ, T,
+                         16 * (jj & 3), jj >> 2, true, lane);
     }
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) {
-      const int r = lrow + p * C::RPP;
-      const int rp = (r & ~31) | swap23(r & 31);
-      *reinterpret_cast<u32x4 *>(Qs + buf * C::QSZ + rp * C::QLD + lch * 8) = qreg[p];
-      *reinterpret_cast<u32x4 *>(Gs + buf * C::QSZ + rp * C::QLD + lch * 8) = greg[p];
-    }
-    if (tid < C::BQ) {
-      Ls[buf * C::BQ + tid] = lreg;
-      Ds[buf * C::BQ + tid] = dreg;
+  // lse / delta of the tile: staged through registers (rows past T: lse = +inf, so p = 0)
+  float lreg = 0.f;
+  auto load_vec = [&](int qt) {
+    if (tid < 2 * C::BQ) {
+      const int qq = qt * C::BQ + (tid & (C::BQ - 1));
+      const bool ok = qq < T;
+      const int qc = ok ? qq : T - 1;
+      lreg = tid < C::BQ ? (ok ? lseb[qc] * kLog2e : INFINITY) : (ok ? delb[qc] : 0.f);
     }
   };
+  auto store_vec = [&](int buf) {
+    if (tid < C::BQ) Ls[buf * C::BQ + tid] = lreg;
+    else if (tid < 2 * C::BQ) Ds[buf * C::BQ + tid - C::BQ] = lreg;
+  };
 
-  gload(qt0);
-  sstore(0);
+  issue_tile(qt0, 0);
+  load_vec(qt0);
+  store_vec(0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int qt = qt0; qt <= qt1; ++qt) {
     const int buf = (qt - qt0) & 1;
-    if (qt < qt1) gload(qt + 1);
+    if (qt < qt1) {
+      issue_tile(qt + 1, buf ^ 1);
+      load_vec(qt + 1);
+    }
     const int qbase = qt * C::BQ;
     const bool active = kw0 <= wk_hi && qbase + C::BQ - 1 >= kw0 && qbase <= wq_hi;
     if (active) {
       const bool need_mask = (qbase < wk_hi) || (window > 0 && qbase + C::BQ - 1 - kw0 >= window);
-      const uint16_t *Qt = Qs + buf * C::QSZ;
-      const uint16_t *Gt = Gs + buf * C::QSZ;
+      const uint16_t *Qt = smem + 2 * buf * C::TSZ;
+      const uint16_t *Gt = Qt + C::TSZ;
       const float *Lt = Ls + buf * C::BQ;
       const float *Dt = Ds + buf * C::BQ;
+      const int rel0 = qbase + 8 * h - my_k;
+      // Two 32-query sub-blocks, software pipelined: the softmax-side VALU work of
+      // one sub-block is placed between independent MFMAs of the other.
+      auto body = [&](auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
+        f32x16 s[2], dp[2];
+        bf16x8 pb[2][2], pl[2][2], sbv[2][2];
+        auto qk = [&](int sb) {  // S = Q K^T, dP = dO V^T, one key per lane
+          s[sb] = f32x16{};
+          dp[sb] = f32x16{};
+          const int row = sb * 32 + ln;
+          bf16x8 qa[C::KST], ga[C::KST];  // all operands requested before the first MFMA
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
-        const uint16_t *qp = Qt + (sb * 32 + ln) * C::QLD + 8 * h;
-        const uint16_t *gp = Gt + (sb * 32 + ln) * C::QLD + 8 * h;
+          for (int st = 0; st < C::KST; ++st) {
+            qa[st] = lds_read_b128(Qt + dt_off<C::BQ>(row, 2 * st + h));
+            ga[st] = lds_read_b128(Gt + dt_off<C::BQ>(row, 2 * st + h));
+          }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) s = mfma32(lds_read_b128(qp + 16 * st), kr[st], s);
+          for (int st = 0; st < C::KST; ++st) {
+            s[sb] = mfma32(qa[st], kr[st], s[sb]);
+            dp[sb] = mfma32(ga[st], vr[st], dp[sb]);
+          }
+        };
+        auto softmax = [&](int sb) {  // P = exp(S - LSE), dS = P (dP - delta)
+          // register 8t + j holds query row sb*32 + 16t + 8h + j
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) dp = mfma32(lds_read_b128(gp + 16 * st), vr[st], dp);
-        // register i holds query row sb*32 + c_row(i, h) = sb*32 + 16*(i/8) + 8h + i%8
+          for (int t = 0; t < 2; ++t) {
+            const int r0 = sb * 32 + 16 * t + 8 * h;
+            const f32x4 l0 = *reinterpret_cast<const f32x4 *>(Lt + r0);
+            const f32x4 l1 = *reinterpret_cast<const f32x4 *>(Lt + r0 + 4);
+            const f32x4 d0 = *reinterpret_cast<const f32x4 *>(Dt + r0);
+            const f32x4 d1 = *reinterpret_cast<const f32x4 *>(Dt + r0 + 4);
+            f32x16 &S = s[sb], &G = dp[sb];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r0 = sb * 32 + 16 * t + 8 * h;
-          const f32x4 l0 = *reinterpret_cast<const f32x4 *>(Lt + r0);
-          const f32x4 l1 = *reinterpret_cast<const f32x4 *>(Lt + r0 + 4);
-          const f32x4 d0 = *reinterpret_cast<const f32x4 *>(Dt + r0);
-          const f32x4 d1 = *reinterpret_cast<const f32x4 *>(Dt + r0 + 4);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int i = 8 * t + j;
-            const float lj = j < 4 ? l0[j] : l1[j - 4];
-            const float dj = j < 4 ? d0[j] : d1[j - 4];
-            float p = fast_exp2(fmaf(s[i], c, -lj));
-            if (need_mask) {
-              const int qq = qbase + r0 + j;
-              const bool vis = my_k <= qq && (window < 0 || qq - my_k < window);
-              if (!vis) p = 0.f;
+            for (int j = 0; j < 8; ++j) {
+              const int i = 8 * t + j;
+              const float lj = j < 4 ? l0[j] : l1[j - 4];
+              const float dj = j < 4 ? d0[j] : d1[j - 4];
+              float p = fast_exp2(fmaf(S[i], c, -lj));
+              if (MASK) p = (unsigned)(rel0 + sb * 32 + 16 * t + j) <= wm1 ? p : 0.f;
+              S[i] = p;
+              G[i] = p * (G[i] - dj);
             }
-            s[i] = p;
-            dp[i] = p * (dp[i] - dj);
+            // P enters dV as bf16 hi + lo (P = hi + lo to ~16 bits): a single bf16 P
+            // leaves |dV| >= 4 outside 2e-2 of the exact gradient.
+            pb[sb][t] = to_bf16x8(S, 8 * t);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pl[sb][t][j] = (__bf16)(S[8 * t + j] - (float)pb[sb][t][j]);
+            sbv[sb][t] = to_bf16x8(G, 8 * t);
           }
-        }
+        };
+        auto grads = [&](int sb) {  // dV^T += dO^T P, dK^T += Q^T dS
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          // P enters dV as bf16 hi + lo (P = hi + lo to ~16 bits): a single bf16 P
-          // leaves |dV| >= 4 outside 2e-2 of the exact gradient.
-          const bf16x8 pb = to_bf16x8(s, 8 * t);
-          bf16x8 pl;
+          for (int t = 0; t < 2; ++t) {
+            bf16x8 gt[C::NDB], qt_[C::NDB];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) pl[j] = (__bf16)(s[8 * t + j] - (float)pb[j]);
-          const bf16x8 sbv = to_bf16x8(dp, 8 * t);
-          const uint16_t *gt = Gt + (sb * 32 + 16 * t) * C::QLD;
-          const uint16_t *qt_ = Qt + (sb * 32 + 16 * t) * C::QLD;
+            for (int d = 0; d < C::NDB; ++d) {
+              gt[d] = dt_read_tr_perm<C::BQ>(Gt, sb * 32 + 16 * t, d, lane);
+              qt_[d] = dt_read_tr_perm<C::BQ>(Qt, sb * 32 + 16 * t, d, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int d = 0; d < D / 32; ++d) {
-            const bf16x8 ga = lds_read_tr_block_perm(gt + 32 * d, C::QLD, lane);
-            dva[d] = mfma32(ga, pb, dva[d]);
-            dva[d] = mfma32(ga, pl, dva[d]);
-            dka[d] = mfma32(lds_read_tr_block_perm(qt_ + 32 * d, C::QLD, lane), sbv, dka[d]);
+            for (int d = 0; d < C::NDB; ++d) {
+              dva[d] = mfma32(gt[d], pb[sb][t], dva[d]);
+              dva[d] = mfma32(gt[d], pl[sb][t], dva[d]);
+              dka[d] = mfma32(qt_[d], sbv[sb][t], dka[d]);
+            }
           }
-        }
-      }
+        };
+        qk(0);
+        qk(1);
+        softmax(0);
+        grads(0);
+        softmax(1);
+        grads(1);
+      };
+      if (need_mask) body(std::true_type{});
+      else body(std::false_type{});
     }
-    if (qt < qt1) sstore(buf ^ 1);
+    if (qt < qt1) store_vec(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
   if (my_k < T) {
     uint16_t *dkb = dk + base, *dvb = dv + base;
 #pragma unroll
-    for (int d = 0; d < D / 32; ++d)
+    for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 pk, pv;
@@ -237,7 +258,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
                 ((uint32_t)f32_to_bf16_bits(dva[d][4 * g + 1]) << 16);
         pv[1] = (uint32_t)f32_to_bf16_bits(dva[d][4 * g + 2]) |
                 ((uint32_t)f32_to_bf16_bits(dva[d][4 * g + 3]) << 16);
-        const size_t off = my_k * rs + 32 * d + 8 * g + 4 * h;
+        const size_t off = (size_t)my_k * rs + 32 * d + 8 * g + 4 * h;
         *reinterpret_cast<u32x2 *>(dkb + off) = pk;
         *reinterpret_cast<u32x2 *>(dvb + off) = pv;
       }
@@ -249,12 +270,10 @@ template <int D>
 struct DqCfg {
   static constexpr int BM = 128;          // queries per workgroup (4 waves x 32)
   static constexpr int BN = 64;           // keys per LDS tile
-  static constexpr int NT = 256;
-  static constexpr int KLD = D + 8;
-  static constexpr int KSZ = BN * KLD;
-  static constexpr int CPR = D / 8;
-  static constexpr int RPP = NT / CPR;
-  static constexpr int PASSES = BN / RPP;
+  static constexpr int TSZ = BN * D;
+  static constexpr int NDB = D / 32;
+  static constexpr int KST = D / 16;
+  static constexpr int CPW = (2 * TSZ * 2 / 1024) / 4;
 };
 
 template <int D>
@@ -264,8 +283,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const float *__restrict__ lse, const float *__restrict__ delta, uint16_t *__restrict__ dq,
     int B, int H, int T, int window, float scale, int nqt) {
   using C = DqCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * C::KSZ];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * C::KSZ];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * C::TSZ];  // [buf][K, V]
 
   const int BH = B * H;
   const int bid = blockIdx.x;
@@ -273,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const int bh = bid % BH;
   const int b = bh / H, hh = bh % H;
   const int q0 = qt * C::BM;
-  const size_t rs = (size_t)H * D;
+  const int rs = H * D;
   const size_t base = ((size_t)b * T * H + hh) * D;
   const uint16_t *qb = q + base, *kb = k + base, *vb = v + base, *gb = dO + base;
 
@@ -287,102 +305,96 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const int kt0 = k_lo / C::BN, kt1 = q_last / C::BN;
   const int wq_lo = qw0, wq_hi = min(T - 1, qw0 + 31);
   const int wk_lo = window > 0 ? wq_lo - window + 1 : 0;
+  // key kk is visible to my_q iff 0 <= my_q - kk <= wm1
+  const unsigned wm1 = window > 0 ? (unsigned)(window - 1) : 0x7fffffffu;
 
-  bf16x8 qr[D / 16], gr[D / 16];
+  bf16x8 qr[C::KST], gr[C::KST];
+  {
+    const int row = min(my_q, T - 1);
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) {
-    if (my_q < T) {
-      qr[st] = *reinterpret_cast<const bf16x8 *>(qb + my_q * rs + 16 * st + 8 * h);
-      gr[st] = *reinterpret_cast<const bf16x8 *>(gb + my_q * rs + 16 * st + 8 * h);
-    } else {
-      qr[st] = bf16x8{};
-      gr[st] = bf16x8{};
+    for (int st = 0; st < C::KST; ++st) {
+      qr[st] = *reinterpret_cast<const bf16x8 *>(qb + (size_t)row * rs + 16 * st + 8 * h);
+      gr[st] = *reinterpret_cast<const bf16x8 *>(gb + (size_t)row * rs + 16 * st + 8 * h);
     }
   }
   const float l2 = my_q < T ? lse[(size_t)bh * T + my_q] * kLog2e : INFINITY;
   const float dl = my_q < T ? delta[(size_t)bh * T + my_q] : 0.f;
   const float c = scale * kLog2e;
 
-  f32x16 acc[D / 32];
+  f32x16 acc[C::NDB];
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d) acc[d] = f32x16{};
+  for (int d = 0; d < C::NDB; ++d) acc[d] = f32x16{};
 
-  u32x4 kreg[C::PASSES], vreg[C::PASSES];
-  const int lrow = tid / C::CPR, lch = tid % C::CPR;
-  auto gload = [&](int kt) {
+  auto issue_tile = [&](int kt, int buf) {
 #pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) {
-      const int key = kt * C::BN + lrow + p * C::RPP;
-      if (key < T) {
-        kreg[p] = ldg16(kb + key * rs + lch * 8);
-        vreg[p] = ldg16(vb + key * rs + lch * 8);
-      } else {
-        kreg[p] = u32x4{};
-        vreg[p] = u32x4{};
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) {
-      const int r = lrow + p * C::RPP;
-      const int rp = (r & ~31) | swap23(r & 31);
-      *reinterpret_cast<u32x4 *>(Ks + buf * C::KSZ + rp * C::KLD + lch * 8) = kreg[p];
-      *reinterpret_cast<u32x4 *>(Vs + buf * C::KSZ + rp * C::KLD + lch * 8) = vreg[p];
+    for (int cc = 0; cc < C::CPW; ++cc) {
+      const int j = w * C::CPW + cc;
+      const int tensor = j / (4 * C::NDB), jj = j % (4 * C::NDB);
+      copy_rows16<C::BN>(smem + (2 * buf + tensor) * C::TSZ, tensor ? vb : kb, rs, kt * C::BN, T,
+                         16 * (jj & 3), jj >> 2, true, lane);
     }
   };
 
-  gload(kt0);
-  sstore(0);
+  issue_tile(kt0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int kt = kt0; kt <= kt1; ++kt) {
     const int buf = (kt - kt0) & 1;
-    if (kt < kt1) gload(kt + 1);
+    if (kt < kt1) issue_tile(kt + 1, buf ^ 1);
     const int kbase = kt * C::BN;
     const bool active = wq_hi >= wq_lo && kbase <= wq_hi && kbase + C::BN - 1 >= wk_lo;
     if (active) {
       const bool need_mask =
           (kbase + C::BN - 1 > wq_lo) || (window > 0 && wq_hi - kbase >= window);
-      const uint16_t *Kt = Ks + buf * C::KSZ;
-      const uint16_t *Vt = Vs + buf * C::KSZ;
+      const uint16_t *Kt = smem + 2 * buf * C::TSZ;
+      const uint16_t *Vt = Kt + C::TSZ;
+      const int rel0 = my_q - kbase - 8 * h;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         f32x16 s = f32x16{}, dp = f32x16{};
-        const uint16_t *kp = Kt + (sb * 32 + ln) * C::KLD + 8 * h;
-        const uint16_t *vp = Vt + (sb * 32 + ln) * C::KLD + 8 * h;
+        const int row = sb * 32 + ln;
+        bf16x8 ka[C::KST], va[C::KST];
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) s = mfma32(lds_read_b128(kp + 16 * st), qr[st], s);
+        for (int st = 0; st < C::KST; ++st) {
+          ka[st] = lds_read_b128(Kt + dt_off<C::BN>(row, 2 * st + h));
+          va[st] = lds_read_b128(Vt + dt_off<C::BN>(row, 2 * st + h));
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) dp = mfma32(lds_read_b128(vp + 16 * st), gr[st], dp);
+        for (int st = 0; st < C::KST; ++st) {
+          s = mfma32(ka[st], qr[st], s);
+          dp = mfma32(va[st], gr[st], dp);
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float p = fast_exp2(fmaf(s[i], c, -l2));
-          if (need_mask) {
-            const int key = kbase + sb * 32 + c_row(i, h);
-            const bool vis = key <= my_q && (window < 0 || my_q - key < window);
-            if (!vis) p = 0.f;
-          }
+          // register i holds key kbase + sb*32 + c_row(i, h) = kbase + 8h + sb*32 + c_row(i, 0)
+          if (need_mask) p = (unsigned)(rel0 - sb * 32 - c_row(i, 0)) <= wm1 ? p : 0.f;
           s[i] = p * (dp[i] - dl);
         }
+        bf16x8 kt_op[2][C::NDB];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int d = 0; d < C::NDB; ++d) kt_op[t][d] = dt_read_tr_perm<C::BN>(Kt, sb * 32 + 16 * t, d, lane);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const bf16x8 dsb = to_bf16x8(s, 8 * t);
-          const uint16_t *kt_ = Kt + (sb * 32 + 16 * t) * C::KLD;
 #pragma unroll
-          for (int d = 0; d < D / 32; ++d)
-            acc[d] = mfma32(lds_read_tr_block_perm(kt_ + 32 * d, C::KLD, lane), dsb, acc[d]);
+          for (int d = 0; d < C::NDB; ++d) acc[d] = mfma32(kt_op[t][d], dsb, acc[d]);
         }
       }
     }
-    if (kt < kt1) sstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
   if (my_q < T) {
     uint16_t *dqb = dq + base;
 #pragma unroll
-    for (int d = 0; d < D / 32; ++d)
+    for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 pk;
@@ -390,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
                 ((uint32_t)f32_to_bf16_bits(acc[d][4 * g + 1] * scale) << 16);
         pk[1] = (uint32_t)f32_to_bf16_bits(acc[d][4 * g + 2] * scale) |
                 ((uint32_t)f32_to_bf16_bits(acc[d][4 * g + 3] * scale) << 16);
-        *reinterpret_cast<u32x2 *>(dqb + my_q * rs + 32 * d + 8 * g + 4 * h) = pk;
+        *reinterpret_cast<u32x2 *>(dqb + (size_t)my_q * rs + 32 * d + 8 * g + 4 * h) = pk;
       }
   }
 }

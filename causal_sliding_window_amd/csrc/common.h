@@ -104,6 +104,67 @@ __device__ __forceinline__ bf16x8 lds_read_tr_block_perm(const uint16_t *base, i
   return cat(lds_read_tr(p), lds_read_tr(p + 8 * ld));
 }
 
+// LDS tiles of R rows x D bf16 are stored d-block-major, [D/32][R][32]: each
+// 32-column block is a sub-tile of 64-byte rows, and inside a row the 16-byte
+// chunk lc (0..3) sits at position lc ^ ((r >> 2) & 3).  Both access patterns
+// used here are free of bank conflicts on the 64 x 4-byte banks: 16 consecutive
+// rows read at one chunk (b128 operand reads) and 4 consecutive rows x one
+// 32-column block (transposed reads by 32 lanes).  For a lane, the XOR term only
+// depends on the lane when the row base is a multiple of 16, so every address is
+// a per-lane base plus a compile-time offset.
+template <int R>
+__device__ __forceinline__ int dt_off(int r, int ch) {  // row r, 16-byte chunk ch (0..D/8-1)
+  return (ch >> 2) * (R * 32) + r * 32 + 8 * ((ch & 3) ^ ((r >> 2) & 3));
+}
+
+// Transposed operand read from a d-block-major tile whose 32-row blocks are stored
+// in swap23 order: delivers tile rows row0 + 8h + 0..7 (row0 % 16 == 0) and the
+// columns 32*db + (lane % 32).
+template <int R>
+__device__ __forceinline__ bf16x8 dt_read_tr_perm(const uint16_t *tile, int row0, int db,
+                                                  int lane) {
+  const int h = lane >> 5, g = (lane >> 4) & 1, i = lane & 15;
+  const int r1 = row0 + 4 * h + (i >> 2), r2 = r1 + 8;
+  const int lc = 2 * g + ((i & 3) >> 1), w = 4 * (i & 1);
+  const uint16_t *sub = tile + db * (R * 32);
+  return cat(lds_read_tr(sub + r1 * 32 + 8 * (lc ^ ((r1 >> 2) & 3)) + w),
+             lds_read_tr(sub + r2 * 32 + 8 * (lc ^ ((r2 >> 2) & 3)) + w));
+}
+
+// Same for a tile stored in natural row order: rows row0 + 8h + 0..3 and + 4..7.
+template <int R>
+__device__ __forceinline__ bf16x8 dt_read_tr(const uint16_t *tile, int row0, int db, int lane) {
+  const int h = lane >> 5, g = (lane >> 4) & 1, i = lane & 15;
+  const int r1 = row0 + 8 * h + (i >> 2), r2 = r1 + 4;
+  const int lc = 2 * g + ((i & 3) >> 1), w = 4 * (i & 1);
+  const uint16_t *sub = tile + db * (R * 32);
+  return cat(lds_read_tr(sub + r1 * 32 + 8 * (lc ^ ((r1 >> 2) & 3)) + w),
+             lds_read_tr(sub + r2 * 32 + 8 * (lc ^ ((r2 >> 2) & 3)) + w));
+}
+
+// Asynchronous 16-byte copy global -> LDS: lane l's 16 bytes land at lds + 16 l
+// (lds must be the same for the whole wave).  Completion is awaited with
+// s_waitcnt vmcnt before the barrier that publishes the tile.
+__device__ __forceinline__ void copy16_to_lds(const void *src, void *lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// Copy of 16 rows of one 32-column block of a row-major bf16 matrix (row stride
+// rs elements, rows clamped to [0, nrows-1]) into a d-block-major LDS tile of R
+// rows: tile rows row16 .. row16+15 of block db.  With perm, tile row r of each
+// 32-row block is placed at LDS row swap23(r) (see dt_read_tr_perm).  One call per
+// wave moves 1 KB.
+template <int R>
+__device__ __forceinline__ void copy_rows16(uint16_t *tile, const uint16_t *src, int rs,
+                                            int row_base, int nrows, int row16, int db,
+                                            bool perm, int lane) {
+  const int r = row16 + (lane >> 2);                 // LDS row
+  const int lc = (lane & 3) ^ ((r >> 2) & 3);        // logical chunk stored at this position
+  const int trow = perm ? ((r & ~31) | swap23(r & 31)) : r;
+  const int grow = min(row_base + trow, nrows - 1);
+  copy16_to_lds(src + (size_t)grow * rs + 32 * db + 8 * lc, tile + db * (R * 32) + row16 * 32);
+}
+
 __device__ __forceinline__ u32x4 ldg16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }

@@ -121,12 +121,21 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       const uint16_t *Kt = Ks + buf * C::KSZ;
       const uint16_t *Vt = Vs + buf * C::VSZ;
       f32x16 s[2];
+      {
+        bf16x8 ka[2][D / 16];  // all K operands requested before the first MFMA
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        s[sb] = f32x16{};
-        const uint16_t *kp = Kt + (sb * 32 + ln) * C::KLD + 8 * h;
+        for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) s[sb] = mfma32(lds_read_b128(kp + 16 * st), qr[st], s[sb]);
+          for (int st = 0; st < D / 16; ++st)
+            ka[sb][st] = lds_read_b128(Kt + (sb * 32 + ln) * C::KLD + 8 * h + 16 * st);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+            if (st == 0) s[sb] = f32x16{};
+            s[sb] = mfma32(ka[sb][st], qr[st], s[sb]);
+          }
       }
       if (need_mask) {
 #pragma unroll
@@ -161,15 +170,21 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 #pragma unroll
       for (int d = 0; d < D / 32; ++d) acc[d] *= alpha;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int sb = 0; sb < 2; ++sb) {
+        bf16x8 va[2][D / 32];  // V^T operands of this 32-key block, requested up front
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int d = 0; d < D / 32; ++d)
+            va[t][d] = lds_read_tr_block(Vt + (sb * 32 + 16 * t) * C::VLD + 32 * d, C::VLD, lane);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const bf16x8 pb = to_bf16x8(s[sb], 8 * t);
-          const uint16_t *vp = Vt + (sb * 32 + 16 * t) * C::VLD;
 #pragma unroll
-          for (int d = 0; d < D / 32; ++d)
-            acc[d] = mfma32(lds_read_tr_block(vp + 32 * d, C::VLD, lane), pb, acc[d]);
+          for (int d = 0; d < D / 32; ++d) acc[d] = mfma32(va[t][d], pb, acc[d]);
         }
+      }
     }
     if (kt < kt1) sstore(buf ^ 1);
     __syncthreads();
