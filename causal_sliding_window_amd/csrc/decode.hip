@@ -2,14 +2,16 @@
 // engine decodes one token per step against the cache its attention kernels
 // read).  Bound by HBM: every visible K/V cache row is read exactly once.
 //
-// decode_split_kernel: workgroup (chunk c, head h, sequence b) reads seqlens[b] on
+// decode_split_kernel: workgroup (head h, chunk c, sequence b) reads seqlens[b] on
 //   the device, takes its kDecodeChunk rows of the visible range
 //   [max(0, L - W), L), and writes a partial (o_c normalised, lse_c) to the
-//   workspace.  Each K/V row of one head is 256 contiguous bytes (bf16, D = 128)
-//   read by D/8 lanes with 16-byte loads; all rows of a chunk are requested before
-//   any is used.
-// decode_merge_kernel: one workgroup per (b, h) combines the partials,
-//   lse = ln sum_c exp(lse_c), o = sum_c exp(lse_c - lse) o_c.
+//   workspace (or o and lse directly when the visible range is one chunk).  Each
+//   K/V row of one head is 256 contiguous bytes (bf16, D = 128) read by D/8 lanes
+//   with non-temporal 16-byte loads; every wave requests all of its rows before
+//   using any.
+// decode_merge_kernel: lse = ln sum_c exp(lse_c), o = sum_c exp(lse_c - lse) o_c.
+//   A separate launch: merging inside the split kernel needs agent-scope fences,
+//   which on this chip write back and invalidate an XCD's whole L2 per workgroup.
 #include "common.h"
 #include "launch.h"
 
@@ -49,133 +51,188 @@ template <typename TT, int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const TT *__restrict__ q, const TT *__restrict__ kc, const TT *__restrict__ vc,
     const int *__restrict__ seqlens, float *__restrict__ ws_o, float *__restrict__ ws_lse,
-    int H, int Tmax, int window, float scale, int nsplit) {
+    TT *__restrict__ o, float *__restrict__ lse, int H, int Tmax, int window, float scale,
+    int nsplit) {
   constexpr int EPL = Elem<TT>::PER16;  // elements per 16-byte load
-  constexpr int LPR = D / EPL;          // lanes per row
-  constexpr int RPP = 256 / LPR;        // rows per pass
-  constexpr int CH = kDecodeChunk;
-  constexpr int PASSES = CH / RPP;
-  constexpr int BATCH = PASSES < 8 ? PASSES : 8;  // rows in flight per thread
-  __shared__ float sc[CH];
-  __shared__ float part[RPP][D + 1];
-  __shared__ float red[8];
+  constexpr int LPR = D / EPL;          // lanes per cache row
+  constexpr int GPW = 64 / LPR;         // rows per wave and round
+  constexpr int CH = kDecodeChunk;      // rows per workgroup
+  constexpr int TPW = CH / 4;           // rows per wave
+  constexpr int ROUNDS = TPW / GPW;
+  __shared__ float part_o[4][D];
+  __shared__ float part_ml[4][2];
 
-  const int c = blockIdx.x, hh = blockIdx.y, b = blockIdx.z;
+  // heads vary fastest across workgroups: the workgroups reading the rows of one
+  // token range (adjacent 256-byte pieces of the same cache lines' DRAM pages) run together
+  const int hh = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+  const int bh = b * H + hh;
   const int L = min(seqlens[b], Tmax);
-  if (L <= 0) return;
+  if (L <= 0) {  // empty sequence: o = 0, lse = -inf
+    if (c == 0) {
+      for (int d = threadIdx.x; d < D; d += blockDim.x) o[(size_t)bh * D + d] = Elem<TT>::pack(0.f);
+      if (lse && threadIdx.x == 0) lse[bh] = -INFINITY;
+    }
+    return;
+  }
   const int lo = visible_lo(L, window);
   const int n = L - lo;
   if (c * CH >= n) return;
   const int t0 = lo + c * CH;
   const int cnt = min(CH, L - t0);
 
-  const int tid = threadIdx.x, r = tid / LPR, sl = tid % LPR;
-  float qf[EPL];
-  Elem<TT>::unpack(ldg16(q + ((size_t)b * H + hh) * D + sl * EPL), qf);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int grp = lane / LPR, sl = lane % LPR;
   const size_t rs = (size_t)H * D;
   const TT *kb = kc + ((size_t)b * Tmax * H + hh) * D + sl * EPL;
   const TT *vb = vc + ((size_t)b * Tmax * H + hh) * D + sl * EPL;
 
-  // scores
-  for (int p0 = 0; p0 < PASSES; p0 += BATCH) {
-    u32x4 kr[BATCH];
+  // Every K and V row of this wave is requested before any is used.  Rows past the
+  // chunk are read clamped to its last row and masked out below.
+  u32x4 kr[ROUNDS], vr[ROUNDS];
 #pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      const int t = (p0 + j) * RPP + r;
-      kr[j] = t < cnt ? ldg16(kb + (size_t)(t0 + t) * rs) : u32x4{};
-    }
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      float kf[EPL];
-      Elem<TT>::unpack(kr[j], kf);
-      float dot = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], kf[e], dot);
-#pragma unroll
-      for (int off = LPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, LPR);
-      const int t = (p0 + j) * RPP + r;
-      if (sl == 0 && t < cnt) sc[t] = dot * scale;
-    }
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int t = min(w * TPW + r * GPW + grp, cnt - 1);
+    kr[r] = ldg16_stream(kb + (size_t)(t0 + t) * rs);
   }
-  __syncthreads();
-
-  // chunk max and sum (CH == blockDim.x)
-  const float x = tid < cnt ? sc[tid] : -INFINITY;
-  float m = x;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((tid & 63) == 0) red[tid >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float pw = tid < cnt ? expf(x - m) : 0.f;
-  float s = pw;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  __syncthreads();  // everyone has read red[0..3]
-  if ((tid & 63) == 0) red[4 + (tid >> 6)] = s;
-  sc[tid] = pw;
-  __syncthreads();
-  const float lsum = (red[4] + red[5]) + (red[6] + red[7]);
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int t = min(w * TPW + r * GPW + grp, cnt - 1);
+    vr[r] = ldg16_stream(vb + (size_t)(t0 + t) * rs);
+  }
+  float qf[EPL];
+  Elem<TT>::unpack(ldg16(q + ((size_t)b * H + hh) * D + sl * EPL), qf);
 
-  // o = sum_t p_t v_t
-  float acc[EPL];
+  // scores of this wave's rows (each lane group holds one row per round)
+  float sc[ROUNDS];
+  float m = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    float kf[EPL];
+    Elem<TT>::unpack(kr[r], kf);
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], kf[e], dot);
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, LPR);
+    const bool ok = w * TPW + r * GPW + grp < cnt;
+    sc[r] = ok ? dot * scale : -INFINITY;
+    m = fmaxf(m, sc[r]);
+  }
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+  const float mu = m == -INFINITY ? 0.f : m;
+  float lsum = 0.f, acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int p0 = 0; p0 < PASSES; p0 += BATCH) {
-    u32x4 vr[BATCH];
 #pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      const int t = (p0 + j) * RPP + r;
-      vr[j] = t < cnt ? ldg16(vb + (size_t)(t0 + t) * rs) : u32x4{};
-    }
+  for (int r = 0; r < ROUNDS; ++r) {
+    const float p = expf(sc[r] - mu);
+    lsum += p;
+    float vf[EPL];
+    Elem<TT>::unpack(vr[r], vf);
 #pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      const int t = (p0 + j) * RPP + r;
-      const float pj = t < cnt ? sc[t] : 0.f;
-      float vf[EPL];
-      Elem<TT>::unpack(vr[j], vf);
+    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+  }
+  // sum over the lane groups of the wave
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pj, vf[e], acc[e]);
+  for (int off = LPR; off < 64; off <<= 1) {
+    lsum += __shfl_xor(lsum, off);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], off);
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) part_o[w][sl * EPL + e] = acc[e];
+    if (sl == 0) {
+      part_ml[w][0] = m;
+      part_ml[w][1] = lsum;
     }
   }
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) part[r][sl * EPL + e] = acc[e];
   __syncthreads();
-  const size_t slot = ((size_t)b * H + hh) * nsplit + c;
-  if (tid < D) {
-    float o = 0.f;
+  // merge the four wave partials (a wave without visible rows has m = -inf, l = 0)
+  const float M = fmaxf(fmaxf(part_ml[0][0], part_ml[1][0]), fmaxf(part_ml[2][0], part_ml[3][0]));
+  float f[4], Ltot = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < RPP; ++rr) o += part[rr][tid];
-    ws_o[slot * D + tid] = o / lsum;
+  for (int i = 0; i < 4; ++i) {
+    f[i] = part_ml[i][0] == -INFINITY ? 0.f : expf(part_ml[i][0] - M);
+    Ltot += f[i] * part_ml[i][1];
   }
-  if (tid == 0) ws_lse[slot] = m + logf(lsum);
+  const size_t slot = (size_t)bh * nsplit + c;
+  const int nch = (n + CH - 1) / CH;
+  if (tid < D) {
+    const float ov = (f[0] * part_o[0][tid] + f[1] * part_o[1][tid] + f[2] * part_o[2][tid] +
+                      f[3] * part_o[3][tid]) / Ltot;
+    if (nch == 1) o[(size_t)bh * D + tid] = Elem<TT>::pack(ov);  // nothing to merge
+    else ws_o[slot * D + tid] = ov;
+  }
+  if (tid == 0) {
+    if (nch > 1) ws_lse[slot] = M + logf(Ltot);
+    else if (lse) lse[bh] = M + logf(Ltot);
+  }
 }
 
+// One workgroup per (b, h) with more than one chunk.  Pass 1: every thread takes
+// chunks tid, tid + 256, ... for the maximum and the sum of exp(lse_c - max).  Pass
+// 2: thread (g, d) accumulates chunks g, g + G, ... of column d (G = 256 / D), with
+// its loads unrolled so they are in flight together; the G sums are added in a
+// fixed order, so the result does not depend on timing.
 template <typename TT, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(
+__global__ __launch_bounds__(256) void decode_merge_kernel(
     const float *__restrict__ ws_o, const float *__restrict__ ws_lse,
-    const int *__restrict__ seqlens, TT *__restrict__ o, float *__restrict__ lse, int H,
-    int Tmax, int window, int nsplit) {
+    const int *__restrict__ seqlens, TT *__restrict__ o, float *__restrict__ lse, int H, int Tmax,
+    int window, int nsplit) {
+  constexpr int G = 256 / D;
+  __shared__ float red[4];
+  __shared__ float part[G][D];
   const int bh = blockIdx.x, b = bh / H;
-  const int tid = threadIdx.x;
   const int L = min(seqlens[b], Tmax);
-  if (L <= 0) {
-    o[(size_t)bh * D + tid] = Elem<TT>::pack(0.f);
-    if (lse && tid == 0) lse[bh] = -INFINITY;
-    return;
-  }
+  if (L <= 0) return;
   const int n = L - visible_lo(L, window);
   const int nch = (n + kDecodeChunk - 1) / kDecodeChunk;
+  if (nch <= 1) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float *ls = ws_lse + (size_t)bh * nsplit;
+
   float m = -INFINITY;
-  for (int c = 0; c < nch; ++c) m = fmaxf(m, ls[c]);
-  float tot = 0.f;
-  for (int c = 0; c < nch; ++c) tot += expf(ls[c] - m);
-  const float lt = m + logf(tot);
+  for (int cc = tid; cc < nch; cc += 256) m = fmaxf(m, ls[cc]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float s = 0.f;
+  for (int cc = tid; cc < nch; cc += 256) s += expf(ls[cc] - M);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) red[w] = s;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+
+  const int g = tid / D, d = tid % D;
+  const float *os = ws_o + (size_t)bh * nsplit * D + d;
   float acc = 0.f;
-  for (int c = 0; c < nch; ++c) acc += expf(ls[c] - lt) * ws_o[((size_t)bh * nsplit + c) * D + tid];
-  o[(size_t)bh * D + tid] = Elem<TT>::pack(acc);
-  if (lse && tid == 0) lse[bh] = lt;
+  int cc = g;
+  for (; cc + 7 * G < nch; cc += 8 * G) {
+    float lv[8], ov[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      lv[u] = ls[cc + u * G];
+      ov[u] = os[(size_t)(cc + u * G) * D];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = fmaf(expf(lv[u] - M), ov[u], acc);
+  }
+  for (; cc < nch; cc += G) acc = fmaf(expf(ls[cc] - M), os[(size_t)cc * D], acc);
+  part[g][d] = acc;
+  __syncthreads();
+  if (tid < D) {
+    float a = part[0][tid];
+#pragma unroll
+    for (int i = 1; i < G; ++i) a += part[i][tid];
+    o[(size_t)bh * D + tid] = Elem<TT>::pack(a / tot);
+    if (lse && tid == 0) lse[bh] = M + logf(tot);
+  }
 }
 
 template <typename TT, int D>
@@ -185,11 +242,12 @@ static hipError_t launch_decode_t(const void *q, const void *k_cache, const void
   const int ns = decode_num_splits(Tmax, window);
   float *ws_o = ws;
   float *ws_lse = ws + (size_t)B * H * ns * D;
-  decode_split_kernel<TT, D><<<dim3(ns, H, B), 256, 0, st>>>(
-      (const TT *)q, (const TT *)k_cache, (const TT *)v_cache, seqlens, ws_o, ws_lse, H, Tmax,
-      window, scale, ns);
-  decode_merge_kernel<TT, D><<<B * H, D, 0, st>>>(ws_o, ws_lse, seqlens, (TT *)o, lse, H, Tmax,
-                                                  window, ns);
+  decode_split_kernel<TT, D><<<dim3(H, ns, B), 256, 0, st>>>(
+      (const TT *)q, (const TT *)k_cache, (const TT *)v_cache, seqlens, ws_o, ws_lse, (TT *)o, lse,
+      H, Tmax, window, scale, ns);
+  if (ns > 1)
+    decode_merge_kernel<TT, D><<<B * H, 256, 0, st>>>(ws_o, ws_lse, seqlens, (TT *)o, lse, H, Tmax,
+                                                      window, ns);
   return hipGetLastError();
 }
 

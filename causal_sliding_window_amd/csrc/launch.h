@@ -7,7 +7,7 @@
 namespace swattn {
 
 // Number of KV rows one decode workgroup handles.
-constexpr int kDecodeChunk = 256;
+constexpr int kDecodeChunk = 128;
 
 int decode_num_splits(int Tmax, int window);
 

@@ -137,7 +137,8 @@ int swattn_bwd_dq_f32(const float *q, const float *k, const float *v, const floa
 /*
  * Decode workspace in bytes: per (sequence, head, KV split) one float32 partial
  * output [D] and one partial LSE.  Depends on Tmax and window because they bound
- * the number of splits.  Returns 0 for invalid sizes.
+ * the number of splits.  Returns 0 for invalid sizes.  No initialisation needed;
+ * calls that may run concurrently need separate workspaces.
  */
 size_t swattn_decode_workspace_size(int B, int H, int D, int Tmax, int window);
 
@@ -148,7 +149,8 @@ size_t swattn_decode_workspace_size(int B, int H, int D, int Tmax, int window);
  * 0 .. L-1 when window < 0).  Rows >= L are never read.  seqlens is read on the
  * device; values above Tmax are clamped to Tmax, and L <= 0 yields o = 0 and
  * lse = -inf.  lse may be NULL.  The visible range is split across workgroups
- * and the partial results are merged by their LSE.
+ * and the partial results are merged by their LSE in a fixed order (bitwise
+ * reproducible).
  */
 int swattn_decode(const void *q, const void *k_cache, const void *v_cache,
                   const int *seqlens, void *o, float *lse, int B, int H, int D,

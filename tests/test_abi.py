@@ -55,9 +55,9 @@ def test_workspace_sizes():
     assert swattn.swattn_bwd_workspace_size(1, 1, 3, 64) == 256
     assert swattn.swattn_bwd_workspace_size(1, 1, 3, 96) == 0
     assert swattn.swattn_bwd_workspace_size(0, 1, 3, 64) == 0
-    # 4096 rows in chunks of 256 -> 16 splits; a 1024 window -> 4
-    assert swattn.swattn_decode_workspace_size(32, 12, 128, 4096, -1) == 32 * 12 * 16 * 129 * 4
-    assert swattn.swattn_decode_workspace_size(32, 12, 128, 4096, 1024) == 32 * 12 * 4 * 129 * 4
+    # 4096 rows in chunks of 128 -> 32 splits; a 1024 window -> 8
+    assert swattn.swattn_decode_workspace_size(32, 12, 128, 4096, -1) == 32 * 12 * 32 * 129 * 4
+    assert swattn.swattn_decode_workspace_size(32, 12, 128, 4096, 1024) == 32 * 12 * 8 * 129 * 4
     assert swattn.swattn_decode_workspace_size(1, 1, 128, 4096, 0) == 0
 
 
