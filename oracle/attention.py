@@ -18,7 +18,7 @@ Sources (the nanochat pages):
   through the kernels' with-KV-cache entry; decode is one new query token per
   sequence against that cache.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
 
 * ``window = W >= 1``: query i sees key j iff ``j <= i`` and ``i - j < W``, i.e. the
   W most recent keys including itself.  ``window < 0`` means full causal.
