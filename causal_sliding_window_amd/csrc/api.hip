@@ -21,6 +21,8 @@ int check_common(int B, int H, int T, int D, int window) {
   const long long rows = (long long)B * T * H;
   if (rows > INT_MAX / 2 || (long long)B * H * ((T + 127) / 128) > INT_MAX / 2)
     return SWATTN_ERR_INVALID_ARG;
+  // buffer loads address one sequence's [T, H, D] block with 32-bit byte offsets
+  if ((long long)(T + 128) * H * D * 2 > INT_MAX) return SWATTN_ERR_UNSUPPORTED;
   return SWATTN_OK;
 }
 

@@ -165,6 +165,22 @@ __device__ __forceinline__ void copy_rows16(uint16_t *tile, const uint16_t *src,
   copy16_to_lds(src + (size_t)grow * rs + 32 * db + 8 * lc, tile + db * (R * 32) + row16 * 32);
 }
 
+// Buffer resource over `nbytes` bytes from `base` (raw addressing, no stride):
+// loads through it at byte offsets >= nbytes return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nbytes,
+                                           0x00020000);
+}
+
+// Asynchronous 16-byte copy through a buffer resource into LDS: lane l's bytes at
+// byte offset voff land at lds + 16 l (lds uniform across the wave); offsets past
+// the resource's size deliver zeros.  Completion: s_waitcnt vmcnt, then a barrier.
+__device__ __forceinline__ void buf_copy16_to_lds(__amdgpu_buffer_rsrc_t r, void *lds,
+                                                  uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                           voff, 0, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 ldg16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }

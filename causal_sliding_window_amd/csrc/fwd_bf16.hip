@@ -5,17 +5,22 @@
 // Attention unification") with the sliding window of its section 1 feature list.
 //
 // Work decomposition (one workgroup = 4 waves = 128 queries of one (b, h)):
-//   * each wave owns 32 queries; its Q block stays in registers as the MFMA
-//     B operand for S^T = K Q^T (32 keys x 32 queries per MFMA tile);
-//   * K and V tiles of 64 keys are staged in LDS, double buffered, loaded with
-//     16-byte coalesced global reads; only tiles that intersect the workgroup's
-//     causal/window band are visited, and a wave skips tiles outside its own band;
-//   * S^T lands with one query per lane, so the online-softmax row statistics are
-//     per lane (plus one cross-half exchange), and P^T feeds O^T = V^T P^T as the
-//     B operand straight from registers (the K rows are stored in swap23 order so
-//     the C and B register orders coincide); V^T comes from transposed LDS reads;
-//   * the element mask is applied only on tiles crossing the diagonal or the
-//     window's lower edge.
+//   * each wave owns 32 queries; its Q block stays in registers as the MFMA B
+//     operand of S^T = K Q^T (32 keys x 32 queries per MFMA tile), so a lane owns
+//     one query and the row statistics are per lane plus one cross-half exchange;
+//   * K and V tiles of 32 keys reach LDS by direct buffer -> LDS copies (no
+//     register staging; rows past T read as zero), d-block-major with a chunk XOR
+//     so that operand reads are free of bank conflicts; K rows in swap23 order so
+//     the C registers of S^T are already the B operand of O^T = V^T P^T;
+//   * K runs one tile ahead of V: while tile j's softmax runs on the vector ALU,
+//     the MFMAs of S for tile j + 1 are issued between its instructions, then
+//     P_j V_j follows.  Each wave only computes the tiles of its own band;
+//   * the running max is only moved (and O rescaled) when a row max grows by
+//     more than 2^8 in exp2 units, which keeps every P below 256;
+//   * the element mask runs only on tiles crossing the diagonal or the window's
+//     lower edge.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -23,17 +28,17 @@ namespace swattn {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BM = 128;          // queries per workgroup
-  static constexpr int BN = 64;           // keys per LDS tile
-  static constexpr int NT = 256;          // threads
-  static constexpr int KLD = D + 8;       // K tile pitch (elements): b128 reads conflict free
-  static constexpr int VLD = D + 32;      // V tile pitch: transposed reads conflict free
-  static constexpr int KSZ = BN * KLD;
-  static constexpr int VSZ = BN * VLD;
-  static constexpr int CPR = D / 8;       // 16-byte chunks per row
-  static constexpr int RPP = NT / CPR;    // rows per load pass
-  static constexpr int PASSES = BN / RPP;
+  static constexpr int BM = 128;               // queries per workgroup (4 waves x 32)
+  static constexpr int BN = 32;                // keys per tile
+  static constexpr int KST = D / 16;           // k-steps of S over D
+  static constexpr int NDB = D / 32;           // 32-column blocks of D
+  static constexpr int TSZ = BN * D;           // elements of one K or V tile
+  static constexpr int RG = BN / 16;           // 16-row groups per 32-column block
+  static constexpr int CPW = TSZ * 2 / 1024 / 4;  // 1-KB copies per wave and tile
 };
+
+// Row-max growth (exp2 units) tolerated before the running max is moved.
+constexpr float kRescaleLog2 = 8.f;
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
@@ -41,8 +46,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
     int B, int H, int T, int window, float scale, int nqt) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * C::KSZ];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * C::VSZ];
+  // [slot][K, V][TSZ]
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * C::TSZ];
 
   const int BH = B * H;
   const int bid = blockIdx.x;
@@ -50,159 +55,281 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int bh = bid % BH;            // consecutive blocks: different heads
   const int b = bh / H, hh = bh % H;
   const int q0 = qt * C::BM;
-  const size_t rs = (size_t)H * D;
+  const int rs = H * D;                // row stride (elements)
   const size_t base = ((size_t)b * T * H + hh) * D;
   const uint16_t *qb = q + base, *kb = k + base, *vb = v + base;
-  uint16_t *ob = o + base;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in an SGPR
   const int h = lane >> 5, ln = lane & 31;
   const int qw0 = q0 + 32 * w;
   const int my_q = qw0 + ln;
 
+  // key tiles of the workgroup and of this wave
   const int q_last = min(T, q0 + C::BM) - 1;
   const int k_lo = window > 0 ? max(0, q0 - window + 1) : 0;
   const int kt0 = k_lo / C::BN, kt1 = q_last / C::BN;
-
+  int wkt0 = 1 << 30, wkt1 = -1;
+  if (qw0 < T) {
+    wkt0 = (window > 0 ? max(0, qw0 - window + 1) : 0) / C::BN;
+    wkt1 = min(T - 1, qw0 + 31) / C::BN;
+  }
   const int wq_lo = qw0, wq_hi = min(T - 1, qw0 + 31);
-  const int wk_lo = window > 0 ? wq_lo - window + 1 : 0;
+  // key kk is visible to my_q iff 0 <= my_q - kk <= wm1
+  const unsigned wm1 = window > 0 ? (unsigned)(window - 1) : 0x7fffffffu;
 
-  bf16x8 qr[D / 16];
+  // Q block (B operand), rows past T read as zero
+  bf16x8 qr[C::KST];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (uint32_t)T * rs * 2);
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) {
-    if (my_q < T) qr[st] = *reinterpret_cast<const bf16x8 *>(qb + my_q * rs + 16 * st + 8 * h);
-    else qr[st] = bf16x8{};
+    for (int st = 0; st < C::KST; ++st)
+      qr[st] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, (my_q * rs + 16 * st + 8 * h) * 2, 0, 0));
   }
 
-  f32x16 acc[D / 32];
+  // Copy j of a tile (1 KB): LDS block db = j / RG, rows 16 (j % RG) .. + 15.
+  // Lane part of the source offset; this wave issues copies CPW w .. CPW w + CPW - 1.
+  const int rl = lane >> 2;                          // LDS row within the 16-row group
+  const int lc = (lane & 3) ^ ((lane >> 4) & 3);     // logical chunk stored at this position
+  const uint32_t klane = (swap23(rl) * rs + 8 * lc) * 2;
+  const uint32_t vlane = (rl * rs + 8 * lc) * 2;
+  auto issue = [&](int tensor, int kt, int slot) {
+    const uint16_t *src = tensor ? vb : kb;
+    const int row0 = kt * C::BN;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(src + (size_t)row0 * rs, (uint32_t)(T - row0) * rs * 2);
+    uint16_t *tile = smem + (2 * slot + tensor) * C::TSZ;
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d) acc[d] = f32x16{};
+    for (int cc = 0; cc < C::CPW; ++cc) {
+      const int j = C::CPW * w + cc;
+      const int db = j / C::RG, row16 = 16 * (j % C::RG);
+      buf_copy16_to_lds(r, tile + db * (C::BN * 32) + row16 * 32,
+                        (tensor ? vlane : klane) + (row16 * rs + 32 * db) * 2);
+    }
+  };
+
+  f32x16 acc[C::NDB];
+#pragma unroll
+  for (int d = 0; d < C::NDB; ++d) acc[d] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const float c = scale * kLog2e;
+  const float thr = kRescaleLog2 / c;
 
-  u32x4 kreg[C::PASSES], vreg[C::PASSES];
-  const int lrow = tid / C::CPR, lch = tid % C::CPR;
-
-  auto gload = [&](int kt) {
+  // S^T of one tile: register i of a lane in half h holds key c_row(i, h),
+  // query = lane % 32.
+  auto qk = [&](const uint16_t *Kt, f32x16 &s) {
+    bf16x8 ka[C::KST];
 #pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) {
-      const int key = kt * C::BN + lrow + p * C::RPP;
-      if (key < T) {
-        kreg[p] = ldg16(kb + key * rs + lch * 8);
-        vreg[p] = ldg16(vb + key * rs + lch * 8);
-      } else {
-        kreg[p] = u32x4{};
-        vreg[p] = u32x4{};
+    for (int st = 0; st < C::KST; ++st) ka[st] = lds_read_b128(Kt + dt_off<C::BN>(ln, 2 * st + h));
+#pragma unroll
+    for (int st = 0; st < C::KST; ++st) s = mfma32(ka[st], qr[st], st ? s : f32x16{});
+  };
+
+  // Online softmax of one tile: masks (MASK), updates m_run / l_run, returns P as
+  // bf16 B operands and whether O must be rescaled by alpha.
+  auto softmax = [&](auto mask_tag, f32x16 &s, int kbase, bf16x8 (&p)[2], float &alpha) -> bool {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if constexpr (MASK) {
+      const int rel0 = my_q - kbase - 8 * h;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((unsigned)(rel0 - c_row(i, 0)) > wm1) s[i] = -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = xhalf_max(mx);
+    const bool need = __builtin_amdgcn_ballot_w64(mx > m_run + thr) != 0;
+    const float m_new = need ? fmaxf(m_run, mx) : m_run;
+    const float mc = (m_new == -INFINITY ? 0.f : m_new) * c;
+    alpha = fast_exp2(m_run * c - mc);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float e = fast_exp2(fmaf(s[i], c, -mc));
+      s[i] = e;
+      psum += e;
+    }
+    l_run = fmaf(l_run, alpha, psum);
+    m_run = m_new;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) p[t] = to_bf16x8(s, 8 * t);
+    return need;
+  };
+
+  // V^T operands of a tile (transposed LDS reads), then O += P V.
+  using VOps = bf16x8[2][C::NDB];
+  auto v_reads = [&](const uint16_t *Vt, VOps &va) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int d = 0; d < C::NDB; ++d) va[t][d] = dt_read_tr<C::BN>(Vt, 16 * t, d, lane);
+  };
+  // O rescale (when some row max moved) and O += P V of a tile.
+  auto finish = [&](bool need, float alpha, const VOps &va, const bf16x8 (&p)[2]) {
+    if (need) {
+#pragma unroll
+      for (int d = 0; d < C::NDB; ++d) acc[d] *= alpha;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int d = 0; d < C::NDB; ++d) acc[d] = mfma32(va[t][d], p[t], acc[d]);
+  };
+
+  // Softmax of tile kt (S in sc) with the S MFMAs of tile kt + 1 (into sn) issued
+  // between its instructions, then O += P V for tile kt.  The order is fixed by
+  // hand: one MFMA, then a slice of the softmax that runs on the vector ALU while
+  // the MFMA executes; sched_barrier keeps the compiler from regrouping them.
+  // All LDS operand reads of the step are issued before the step's copies into
+  // LDS start (`issue_loads`), so no read has to wait for those copies.
+  auto step = [&](auto mask_tag, auto issue_loads, const uint16_t *Kn, const uint16_t *Vt,
+                  int kbase, f32x16 &sc, f32x16 &sn) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    static_assert(C::KST == 8 || C::KST == 4, "");
+    bf16x8 ka[C::KST];
+#pragma unroll
+    for (int st = 0; st < C::KST; ++st) ka[st] = lds_read_b128(Kn + dt_off<C::BN>(ln, 2 * st + h));
+    VOps va;
+    v_reads(Vt, va);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_loads();
+    __builtin_amdgcn_sched_barrier(0);
+    int st = 0;
+    // an empty asm use keeps a slice's result from drifting to its later uses
+    auto pin = [](float x) {
+      asm volatile("" ::"v"(x));
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto mfma_next = [&] {
+      sn = mfma32(ka[st], qr[st], st ? sn : f32x16{});
+      ++st;
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // slice 1: mask, row max
+    mfma_next();
+    if constexpr (MASK) {
+      const int rel0 = my_q - kbase - 8 * h;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((unsigned)(rel0 - c_row(i, 0)) > wm1) sc[i] = -INFINITY;
+    }
+    float mx = fmaxf(sc[0], sc[1]);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+    pin(mx);
+    // slice 2: cross-half max, rescale decision
+    mfma_next();
+    mx = xhalf_max(mx);
+    const bool need = __builtin_amdgcn_ballot_w64(mx > m_run + thr) != 0;
+    const float m_new = need ? fmaxf(m_run, mx) : m_run;
+    const float mc = (m_new == -INFINITY ? 0.f : m_new) * c;
+    const float alpha = fast_exp2(m_run * c - mc);
+    pin(mc);
+    // slices 3..: exponentials and their sum, 16 / (KST - 3) per slice, then P
+    float psum = 0.f;
+    constexpr int NE = C::KST == 8 ? 4 : 8;   // exponentials per slice
+#pragma unroll
+    for (int e0 = 0; e0 < 16; e0 += NE) {
+      mfma_next();
+#pragma unroll
+      for (int i = e0; i < e0 + NE; ++i) {
+        const float e = fast_exp2(fmaf(sc[i], c, -mc));
+        sc[i] = e;
+        psum += e;
       }
+      pin(psum);
     }
-  };
-  auto sstore = [&](int buf) {
+    bf16x8 p[2];
+    while (st < C::KST) mfma_next();
 #pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) {
-      const int r = lrow + p * C::RPP;
-      const int rk = (r & ~31) | swap23(r & 31);
-      *reinterpret_cast<u32x4 *>(Ks + buf * C::KSZ + rk * C::KLD + lch * 8) = kreg[p];
-      *reinterpret_cast<u32x4 *>(Vs + buf * C::VSZ + r * C::VLD + lch * 8) = vreg[p];
-    }
+    for (int t = 0; t < 2; ++t) p[t] = to_bf16x8(sc, 8 * t);
+    l_run = fmaf(l_run, alpha, psum);
+    m_run = m_new;
+    __builtin_amdgcn_sched_barrier(0);
+    finish(need, alpha, va, p);
   };
 
-  gload(kt0);
-  sstore(0);
+  // Tile pipeline.  K of tile t and V of tile t live in LDS slot (t - kt0) & 1; K
+  // runs one tile ahead, so in step kt the copies of K[kt + 2] (over K[kt], read in
+  // step kt - 1) and V[kt + 1] (over V[kt - 1]) are issued, and they are awaited
+  // at the end of the step.  Every wave runs one barrier per
+  // tile of the workgroup; the phases below only differ in what a wave computes.
+  auto loads = [&](int kt) {
+    const int slot = (kt - kt0) & 1;
+    if (kt + 2 <= kt1) issue(0, kt + 2, slot);
+    if (kt + 1 <= kt1) issue(1, kt + 1, slot ^ 1);
+  };
+  auto k_next = [&](int kt) { return smem + 2 * (((kt - kt0) & 1) ^ 1) * C::TSZ; };
+  auto v_cur = [&](int kt) { return smem + (2 * ((kt - kt0) & 1) + 1) * C::TSZ; };
+  auto sync = [&] {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  // prologue: K, V of tile kt0 and K of kt0 + 1
+  issue(0, kt0, 0);
+  issue(1, kt0, 0);
+  if (kt0 < kt1) issue(0, kt0 + 1, 1);
+  sync();
+  f32x16 sc, sn;
+  if (wkt0 == kt0) qk(smem, sc);
   __syncthreads();
 
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const int buf = (kt - kt0) & 1;
-    if (kt < kt1) gload(kt + 1);
-    const int kbase = kt * C::BN;
-    const bool active = wq_hi >= wq_lo && kbase <= wq_hi && kbase + C::BN - 1 >= wk_lo;
-    if (active) {
-      const bool need_mask =
-          (kbase + C::BN - 1 > wq_lo) || (window > 0 && wq_hi - kbase >= window);
-      const uint16_t *Kt = Ks + buf * C::KSZ;
-      const uint16_t *Vt = Vs + buf * C::VSZ;
-      f32x16 s[2];
-      {
-        bf16x8 ka[2][D / 16];  // all K operands requested before the first MFMA
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int st = 0; st < D / 16; ++st)
-            ka[sb][st] = lds_read_b128(Kt + (sb * 32 + ln) * C::KLD + 8 * h + 16 * st);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st)
-#pragma unroll
-          for (int sb = 0; sb < 2; ++sb) {
-            if (st == 0) s[sb] = f32x16{};
-            s[sb] = mfma32(ka[sb][st], qr[st], s[sb]);
-          }
-      }
-      if (need_mask) {
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kbase + sb * 32 + c_row(i, h);
-            const bool vis = key <= my_q && (window < 0 || my_q - key < window);
-            if (!vis) s[sb][i] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
-      mx = xhalf_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float mc = (m_new == -INFINITY ? 0.f : m_new) * c;
-      const float alpha = fast_exp2(m_run * c - mc);
-      float psum = 0.f;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(s[sb][i], c, -mc));
-          s[sb][i] = p;
-          psum += p;
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < D / 32; ++d) acc[d] *= alpha;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        bf16x8 va[2][D / 32];  // V^T operands of this 32-key block, requested up front
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int d = 0; d < D / 32; ++d)
-            va[t][d] = lds_read_tr_block(Vt + (sb * 32 + 16 * t) * C::VLD + 32 * d, C::VLD, lane);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 pb = to_bf16x8(s[sb], 8 * t);
-#pragma unroll
-          for (int d = 0; d < D / 32; ++d) acc[d] = mfma32(va[t][d], pb, acc[d]);
-        }
-      }
-    }
-    if (kt < kt1) sstore(buf ^ 1);
-    __syncthreads();
+  // Tiles [wkt0, mlim) cross the window's lower edge and need the element mask;
+  // the wave's last tile (wkt1) holds its diagonal.
+  const int mlim = (window > 0 && wq_hi - window >= 0) ? (wq_hi - window) / C::BN + 1 : 0;
+  int kt = kt0;
+  for (; kt < min(wkt0 - 1, kt1 + 1); ++kt) {  // before the wave's band (or all tiles)
+    loads(kt);
+    sync();
+  }
+  if (wkt0 > kt0 && kt == wkt0 - 1) {  // S of the wave's first tile
+    loads(kt);
+    qk(k_next(kt), sc);
+    sync();
+    ++kt;
+  }
+  for (; kt < min(wkt1, mlim); ++kt) {
+    step(std::true_type{}, [&] { loads(kt); }, k_next(kt), v_cur(kt), kt * C::BN, sc, sn);
+    sc = sn;
+    sync();
+  }
+  for (; kt < wkt1; ++kt) {
+    step(std::false_type{}, [&] { loads(kt); }, k_next(kt), v_cur(kt), kt * C::BN, sc, sn);
+    sc = sn;
+    sync();
+  }
+  if (kt == wkt1) {  // the diagonal tile: no S to compute ahead
+    VOps va;
+    v_reads(v_cur(kt), va);
+    __builtin_amdgcn_sched_barrier(0);
+    loads(kt);
+    bf16x8 p[2];
+    float alpha;
+    const bool need = softmax(std::true_type{}, sc, kt * C::BN, p, alpha);
+    finish(need, alpha, va, p);
+    sync();
+    ++kt;
+  }
+  for (; kt <= kt1; ++kt) {  // after the wave's band
+    loads(kt);
+    sync();
   }
 
   const float l_tot = xhalf_sum(l_run);
   if (my_q < T) {
     const float inv = 1.f / l_tot;
+    uint16_t *orow = o + base + (size_t)my_q * rs;
 #pragma unroll
-    for (int d = 0; d < D / 32; ++d)
+    for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        u32x2 pk;
-        pk[0] = (uint32_t)f32_to_bf16_bits(acc[d][4 * g] * inv) |
-                ((uint32_t)f32_to_bf16_bits(acc[d][4 * g + 1] * inv) << 16);
-        pk[1] = (uint32_t)f32_to_bf16_bits(acc[d][4 * g + 2] * inv) |
-                ((uint32_t)f32_to_bf16_bits(acc[d][4 * g + 3] * inv) << 16);
-        *reinterpret_cast<u32x2 *>(ob + my_q * rs + 32 * d + 8 * g + 4 * h) = pk;
+        bf16x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[d][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4 *>(orow + 32 * d + 8 * g + 4 * h) = pk;
       }
     if (h == 0) lse[(size_t)bh * T + my_q] = m_run * scale + logf(l_tot);
   }
@@ -210,7 +337,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                            int B, int H, int T, int D, int window, float scale, hipStream_t st) {
-  const int nqt = (T + 127) / 128;
+  const int nqt = (T + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
   dim3 grid((unsigned)(nqt * B * H)), block(256);
   if (D == 128)
     fwd_bf16_kernel<128><<<grid, block, 0, st>>>((const uint16_t *)q, (const uint16_t *)k,

@@ -44,7 +44,9 @@
  *   SWATTN_ERR_INVALID_ARG  NULL required pointer, B/H/T/D/Tmax <= 0, window == 0,
  *                           a size product that does not fit the kernels' 32-bit
  *                           grid/row indices, or a workspace pointer of NULL
- *   SWATTN_ERR_UNSUPPORTED  D not in {64, 128}
+ *   SWATTN_ERR_UNSUPPORTED  D not in {64, 128}, or (for the training calls) one
+ *                           sequence's [T + 128, H, D] block of 2-byte elements
+ *                           exceeding 2^31 - 1 bytes (32-bit buffer offsets)
  *   SWATTN_ERR_HIP          the HIP runtime reported an error at launch
  * On an error nothing has been enqueued (argument errors) or the state of the
  * outputs is unspecified (HIP errors).

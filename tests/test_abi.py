@@ -73,6 +73,7 @@ MISALIGNED = ctypes.c_void_p((1 << 20) + 2)
     ((None, FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 64, -1, 1.0, None), 1),       # NULL q
     ((FAKE, FAKE, FAKE, FAKE, None, 1, 1, 8, 64, -1, 1.0, None), 1),       # NULL lse
     ((FAKE, MISALIGNED, FAKE, FAKE, FAKE, 1, 1, 8, 64, -1, 1.0, None), 1),  # misaligned k
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1 << 23, 128, -1, 1.0, None), 2),  # 2 GiB sequence
 ])
 def test_fwd_argument_errors(args, expect):
     lib = swattn.lib()
