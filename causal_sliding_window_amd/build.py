@@ -10,27 +10,29 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libswattn.so")
-SOURCES = ["api.hip", "fwd_bf16.hip", "bwd_bf16.hip", "decode.hip", "f32.hip"]
+SOURCES = ["api.hip", "fwd_bf16.hip", "bwd_bf16.hip", "dkdv_bf16.hip", "decode.hip", "f32.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # no packed-fp32 instructions anywhere (they are avoided on this hardware)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # keep MFMA results in arch VGPRs where they feed VALU work: avoids the
-    # accumulator <-> VGPR copies the default form generates
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
+# Per-source extra flags.  Most kernels keep MFMA results in arch VGPRs, where
+# they feed ALU work (avoids accumulator <-> VGPR copies); the dK/dV kernel keeps
+# its accumulators in AGPRs, leaving the arch VGPRs to its operands.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+EXTRA_FLAGS = {s: VGPR_FORM for s in SOURCES if s != "dkdv_bf16.hip"}
 
 
 def hipcc() -> str:
@@ -40,21 +42,37 @@ def hipcc() -> str:
     return exe
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+def build(verbose: bool = False, csrc: str = CSRC, out: str = LIB) -> str:
+    """Compile every source to an object (in parallel), then link the library."""
     noise = "not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    with tempfile.TemporaryDirectory(prefix="swattn_build_") as tmpdir:
+        procs, objs = [], []
+        for s in [s for s in SOURCES if os.path.exists(os.path.join(csrc, s))]:
+            obj = os.path.join(tmpdir, s + ".o")
+            cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(s, []), "-I", INCLUDE, "-I", csrc, "-c",
+                   os.path.join(csrc, s), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((s, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                              text=True)))
+            objs.append(obj)
+        errors = []
+        for s, p in procs:
+            _, err = p.communicate()
+            err = "\n".join(l for l in err.splitlines() if noise not in l)
+            if p.returncode != 0:
+                errors.append(f"{s}: hipcc failed ({p.returncode}):\n{err}")
+            elif verbose and err.strip():
+                print(err, file=sys.stderr)
+        if errors:
+            raise RuntimeError("\n".join(errors))
+        tmp = out + ".tmp"
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed ({res.returncode}):\n{res.stderr}")
+        os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
