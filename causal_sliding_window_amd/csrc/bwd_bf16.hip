@@ -77,7 +77,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const size_t base = ((size_t)b * T * H + hh) * D;
   const uint16_t *qb = q + base, *kb = k + base, *vb = v + base, *gb = dO + base;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in an SGPR
   const int h = lane >> 5, ln = lane & 31;
   const int qw0 = q0 + 32 * w;
   const int my_q = qw0 + ln;
@@ -107,13 +108,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
 #pragma unroll
   for (int d = 0; d < C::NDB; ++d) acc[d] = f32x16{};
 
+  // K and V tiles (rows in swap23 order, d-block-major; rows past T read as zero
+  // and are masked) by buffer -> LDS copies.  Piece j (1 KB): tensor j / (4 NDB),
+  // LDS block db = (j % (4 NDB)) / 4, rows 16 (j % 4) .. + 15.
+  const int rl = lane >> 2;
+  const int lc = (lane & 3) ^ ((lane >> 4) & 3);  // logical chunk stored at this position
+  const uint32_t lane_off = (swap23(rl) * rs + 8 * lc) * 2;
   auto issue_tile = [&](int kt, int buf) {
+    const int row0 = kt * C::BN;
+    const uint32_t nbytes = (uint32_t)(T - row0) * rs * 2;
 #pragma unroll
     for (int cc = 0; cc < C::CPW; ++cc) {
       const int j = w * C::CPW + cc;
       const int tensor = j / (4 * C::NDB), jj = j % (4 * C::NDB);
-      copy_rows16<C::BN>(smem + (2 * buf + tensor) * C::TSZ, tensor ? vb : kb, rs, kt * C::BN, T,
-                         16 * (jj & 3), jj >> 2, true, lane);
+      const int db = jj >> 2, row16 = 16 * (jj & 3);
+      const __amdgpu_buffer_rsrc_t r = make_rsrc((tensor ? vb : kb) + (size_t)row0 * rs, nbytes);
+      buf_copy16_to_lds(r, smem + (2 * buf + tensor) * C::TSZ + db * (C::BN * 32) + row16 * 32,
+                        lane_off + (row16 * rs + 32 * db) * 2);
     }
   };
 
@@ -155,11 +166,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
           if (need_mask) p = (unsigned)(rel0 - sb * 32 - c_row(i, 0)) <= wm1 ? p : 0.f;
           s[i] = p * (dp[i] - dl);
         }
+        // K^T operands: one asm block, so the copies of the next tile stay in flight
         bf16x8 kt_op[2][C::NDB];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int d = 0; d < C::NDB; ++d) kt_op[t][d] = dt_read_tr_perm<C::BN>(Kt, sb * 32 + 16 * t, d, lane);
+        dt_read_tr_perm_block<C::BN, C::NDB>(Kt, sb * 32, lane, kt_op);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {

@@ -142,6 +142,81 @@ __device__ __forceinline__ bf16x8 dt_read_tr(const uint16_t *tile, int row0, int
              lds_read_tr(sub + r2 * 32 + 8 * (lc ^ ((r2 >> 2) & 3)) + w));
 }
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// All 2 * NDB transposed operands ops[t][d] of one 32-row block of a d-block-major
+// tile of R rows stored in swap23 order (what dt_read_tr_perm<R>(tile, row0 + 16 t,
+// d, lane) returns; row0 % 32 == 0), read by one asm block that also waits for
+// them (s_waitcnt lgkmcnt(0) inside).  Reason: the compiler makes every
+// transposed-read builtin wait for all global -> LDS copies in flight, which would
+// cut short the prefetch of the next tile; these reads do not touch the tiles being
+// copied.  Outputs are early-clobber, so no address register is overwritten by a
+// read still in flight.
+template <int R, int NDB>
+__device__ __forceinline__ void dt_read_tr_perm_block(const uint16_t *tile, int row0, int lane,
+                                                      bf16x8 (&ops)[2][NDB]) {
+  static_assert(NDB == 4 || NDB == 2, "D = 128 or 64");
+  const int h = lane >> 5, g = (lane >> 4) & 1, i = lane & 15;
+  const int lc = 2 * g + ((i & 3) >> 1), w = 4 * (i & 1);
+  const int r1 = 4 * h + (i >> 2);  // rows of the first read (+ row0); second read: + 8
+  const uint32_t base = lds_addr(tile) + (uint32_t)row0 * 64;
+  const uint32_t a1 = base + 2 * (r1 * 32 + 8 * (lc ^ h) + w);
+  const uint32_t a2 = base + 2 * ((r1 + 8) * 32 + 8 * (lc ^ (h + 2)) + w);
+  constexpr int DS = 64 * R;  // bytes between 32-column blocks
+  i16x4 r[4 * NDB];
+  if constexpr (NDB == 4) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:%18\n\t"
+        "ds_read_b64_tr_b16 %1, %17 offset:%18\n\t"
+        "ds_read_b64_tr_b16 %2, %16 offset:%19\n\t"
+        "ds_read_b64_tr_b16 %3, %17 offset:%19\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %6, %16 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %7, %17 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %10, %16 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %11, %17 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %12, %16 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %13, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %14, %16 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %15, %17 offset:%25\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+          "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+          "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+        : "v"(a1), "v"(a2), "i"(0), "i"(DS), "i"(2 * DS), "i"(3 * DS), "i"(1024),
+          "i"(1024 + DS), "i"(1024 + 2 * DS), "i"(1024 + 3 * DS)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %1, %9 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %7, %9 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+          "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a1), "v"(a2), "i"(0), "i"(DS), "i"(1024), "i"(1024 + DS)
+        : "memory");
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      const int k = 2 * (t * NDB + d);
+      ops[t][d] = cat(__builtin_bit_cast(bf16x4, r[k]), __builtin_bit_cast(bf16x4, r[k + 1]));
+    }
+}
+
 // Asynchronous 16-byte copy global -> LDS: lane l's 16 bytes land at lds + 16 l
 // (lds must be the same for the whole wave).  Completion is awaited with
 // s_waitcnt vmcnt before the barrier that publishes the tile.

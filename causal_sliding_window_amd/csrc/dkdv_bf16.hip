@@ -208,15 +208,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // One pipeline step for tile qt (S, dP in sc, dpc): the transposed operand reads
-  // of tile qt come first (before any copy is in flight: the compiler makes a
-  // transposed read wait for all outstanding global -> LDS copies), then the
-  // copies of tile qt + 2 start; the S / dP MFMAs of tile qt + 1 (when NEXT) are
-  // issued one by one between the slices of the gradient-side ALU work of tile qt,
-  // and the dV / dK MFMAs of tile qt close the step.
+  // One pipeline step for tile qt (S, dP in sc, dpc).  LDS reads first: the
+  // operands of tile qt + 1's S / dP MFMAs (needed first), then the transposed
+  // operands of tile qt, all before the copies of tile qt + 2 start (the compiler
+  // makes a transposed read wait for every global -> LDS copy in flight).  The S /
+  // dP MFMAs of tile qt + 1 (when NEXT) are issued one by one between the slices
+  // of the gradient-side ALU work of tile qt, and the dV / dK MFMAs of tile qt
+  // close the step.
   auto step = [&](auto mask_tag, auto next_tag, int qt, f32x16 &sc, f32x16 &dpc, f32x16 &sn,
                   f32x16 &dpn) {
     constexpr bool NEXT = decltype(next_tag)::value;
+    const int rel0 = qt * C::BQ + 8 * h - my_k;
+    bf16x8 qa[C::KST], ga[C::KST];
+    if constexpr (NEXT) {
+      const uint16_t *Qn = q_tile(qt + 1), *Gn = Qn + C::TSZ;
+#pragma unroll
+      for (int st = 0; st < C::KST; ++st) {
+        qa[st] = lds_read_b128(Qn + dt_off<C::BQ>(ln, 2 * st + h));
+        ga[st] = lds_read_b128(Gn + dt_off<C::BQ>(ln, 2 * st + h));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     TOps gt, qtr;
     tr_reads(qt, gt, qtr);
     f32x4 L[4], Dl[4];
@@ -224,16 +236,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);
     if (qt + 2 <= qt1) issue(qt + 2);
     __builtin_amdgcn_sched_barrier(0);
-    const int rel0 = qt * C::BQ + 8 * h - my_k;
     if constexpr (NEXT) {
-      const uint16_t *Qn = q_tile(qt + 1), *Gn = Qn + C::TSZ;
-      bf16x8 qa[C::KST], ga[C::KST];
-#pragma unroll
-      for (int st = 0; st < C::KST; ++st) {
-        qa[st] = lds_read_b128(Qn + dt_off<C::BQ>(ln, 2 * st + h));
-        ga[st] = lds_read_b128(Gn + dt_off<C::BQ>(ln, 2 * st + h));
-      }
-      __builtin_amdgcn_sched_barrier(0);
       constexpr int EPS = 16 / C::KST;  // elements per slice
 #pragma unroll
       for (int st = 0; st < C::KST; ++st) {
