@@ -3,8 +3,8 @@
 
 A step is one forward + backward of causal attention on the "small" training
 workload (B8 H6 T2048 D128, bf16, full causal; seeded synthetic data), issued as
-the library's four kernels in order (forward, delta preprocess, dK/dV pass,
-dQ pass).  ``value`` is window-masked TFLOP/s of the whole step: forward
+the library's three kernels in order (forward; dQ pass, which also computes
+delta; dK/dV pass), exactly what swattn_fwd + swattn_bwd launch.  ``value`` is window-masked TFLOP/s of the whole step: forward
 4*D*N_vis*B*H, backward 2.5x that (the usual five-product accounting), with
 N_vis = sum_i min(i+1, W) visible (query, key) pairs per head.
 
@@ -63,12 +63,14 @@ def train_accounting(B, H, T, D, W, elem=2):
         "flops_fwd": 4 * D * n,
         "flops_bwd": 10 * D * n,
         # algorithmic products per kernel: forward S, PV; dK/dV pass S, dP, dV, dK;
-        # dQ pass S, dP, dQ (2*D flops per visible pair each)
-        "kernel_flops": {"fwd": 4 * D * n, "bwd_dkdv": 8 * D * n, "bwd_dq": 6 * D * n,
-                         "bwd_pre": 2 * B * T * H * D},
+        # dQ pass S, dP, dQ (2*D flops per visible pair each) plus delta = dO . o
+        "kernel_flops": {"fwd": 4 * D * n, "bwd_dkdv": 8 * D * n,
+                         "bwd_dq": 6 * D * n + 2 * B * T * H * D},
         # algorithmic HBM bytes per kernel: every operand read once, result written once
-        "kernel_bytes": {"fwd": 4 * act + vec, "bwd_pre": 2 * act + vec,
-                         "bwd_dkdv": 6 * act + 2 * vec, "bwd_dq": 5 * act + 2 * vec},
+        # (dQ pass: q, k, v, o, dO, lse in; dq, delta out.  dK/dV: q, k, v, dO, lse,
+        # delta in; dk, dv out)
+        "kernel_bytes": {"fwd": 4 * act + vec, "bwd_dkdv": 6 * act + 2 * vec,
+                         "bwd_dq": 6 * act + 2 * vec},
     }
 
 
@@ -112,29 +114,27 @@ def bench_training(torch, swattn, inputs, cfg_name, steps, warmup):
         check(lib.swattn_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, T, D, W, scale, sh), "fwd")
         if ev is not None:
             ev[1].record(stream)
-        check(lib.swattn_bwd_preprocess(P(o), P(do), P(ws), B, H, T, D, sh), "bwd_pre")
+        # swattn_bwd is exactly these two passes; the dQ pass also writes delta
+        check(lib.swattn_bwd_dq(P(q), P(k), P(v), P(o), P(do), P(lse), P(ws), P(dq), B, H, T, D, W,
+                                scale, sh), "bwd_dq")
         if ev is not None:
             ev[2].record(stream)
         check(lib.swattn_bwd_dkdv(P(q), P(k), P(v), P(do), P(lse), P(ws), P(dk), P(dv), B, H, T, D,
                                   W, scale, sh), "bwd_dkdv")
         if ev is not None:
             ev[3].record(stream)
-        check(lib.swattn_bwd_dq(P(q), P(k), P(v), P(do), P(lse), P(ws), P(dq), B, H, T, D, W,
-                                scale, sh), "bwd_dq")
-        if ev is not None:
-            ev[4].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    names = ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"]
+    names = ["fwd", "bwd_dq", "bwd_dkdv"]
     per = {n: statistics.fmean(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
     return {"B": B, "H": H, "T": T, "D": D, "W": W, "wall_s": wall, "kernel_ms": per,
             "acct": train_accounting(B, H, T, D, W)}
@@ -255,7 +255,7 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
     pick = lambda d, key: next((v for k, v in d.items() if key in k), None)  # noqa: E731
     copy_f = pick(fe, "copy") or pick(fe, "elementwise")
     copy_w = pick(wr, "copy") or pick(wr, "elementwise")
-    names = {"fwd": "fwd_bf16_kernel", "bwd_pre": "bwd_pre_bf16_kernel",
+    names = {"fwd": "fwd_bf16_kernel",
              "bwd_dkdv": "bwd_dkdv_bf16_kernel", "bwd_dq": "bwd_dq_bf16_kernel",
              "decode_split": "decode_split_kernel"}
     out = {"source_hash": source_hash(), "copy_bytes": copy_bytes,
@@ -317,7 +317,7 @@ def main():
         f, by = acct["kernel_flops"][n], acct["kernel_bytes"][n]
         kernels[n] = {"ms": round(ms, 4), "TFLOP_per_s": round(f / (ms * 1e-3) / 1e12, 1),
                       "GB_per_s": round(by / (ms * 1e-3) / 1e9, 1)}
-    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: tr["kernel_ms"][n])
+    dom = max(tr["kernel_ms"], key=lambda n: tr["kernel_ms"][n])
     dom_ms = tr["kernel_ms"][dom]
     achieved = acct["kernel_flops"][dom] / (dom_ms * 1e-3) / 1e12
     log(f"step {ms_step:.3f} ms, {value:.1f} TFLOP/s; kernels {kernels}")

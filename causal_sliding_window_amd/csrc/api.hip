@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 101;  // 0.1.1: swattn_bwd_dq takes o and writes delta
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -63,10 +63,14 @@ hipError_t launch_bwd_dkdv(bool bf16, const void *q, const void *k, const void *
                              window, scale, st);
 }
 
-hipError_t launch_bwd_dq(bool bf16, const void *q, const void *k, const void *v, const void *dO,
-                         const float *lse, const float *delta, void *dq, int B, int H, int T,
-                         int D, int window, float scale, hipStream_t st) {
-  if (bf16) return launch_bwd_dq_bf16(q, k, v, dO, lse, delta, dq, B, H, T, D, window, scale, st);
+hipError_t launch_bwd_dq(bool bf16, const void *q, const void *k, const void *v, const void *o,
+                         const void *dO, const float *lse, float *delta, void *dq, int B, int H,
+                         int T, int D, int window, float scale, hipStream_t st) {
+  if (bf16)
+    return launch_bwd_dq_bf16(q, k, v, o, dO, lse, delta, dq, B, H, T, D, window, scale, st);
+  // fp32: delta by its own kernel, then the dQ pass
+  hipError_t e = launch_bwd_pre_f32((const float *)o, (const float *)dO, delta, B, H, T, D, st);
+  if (e != hipSuccess) return e;
   return launch_bwd_dq_f32((const float *)q, (const float *)k, (const float *)v,
                            (const float *)dO, lse, delta, (float *)dq, B, H, T, D, window, scale,
                            st);
@@ -83,13 +87,13 @@ int bwd_all(bool bf16, const void *q, const void *k, const void *v, const void *
   if (s != SWATTN_OK) return s;
   if (!all_aligned({q, k, v, o, dO, dq, dk, dv, workspace}) || lse == nullptr)
     return SWATTN_ERR_INVALID_ARG;
+  // the dQ pass also writes delta, which the dK/dV pass then reads
   float *delta = (float *)workspace;
-  hipError_t e = swattn::launch_bwd_pre(bf16, o, dO, delta, B, H, T, D, st);
+  hipError_t e =
+      swattn::launch_bwd_dq(bf16, q, k, v, o, dO, lse, delta, dq, B, H, T, D, window, scale, st);
   if (e == hipSuccess)
     e = swattn::launch_bwd_dkdv(bf16, q, k, v, dO, lse, delta, dk, dv, B, H, T, D, window, scale,
                                 st);
-  if (e == hipSuccess)
-    e = swattn::launch_bwd_dq(bf16, q, k, v, dO, lse, delta, dq, B, H, T, D, window, scale, st);
   return hip_status(e);
 }
 
@@ -112,13 +116,14 @@ int bwd_dkdv(bool bf16, const void *q, const void *k, const void *v, const void 
                                             dv, B, H, T, D, window, scale, st));
 }
 
-int bwd_dq(bool bf16, const void *q, const void *k, const void *v, const void *dO,
-           const float *lse, const void *workspace, void *dq, int B, int H, int T, int D,
-           int window, float scale, hipStream_t st) {
+int bwd_dq(bool bf16, const void *q, const void *k, const void *v, const void *o,
+           const void *dO, const float *lse, void *workspace, void *dq, int B, int H, int T,
+           int D, int window, float scale, hipStream_t st) {
   int s = check_common(B, H, T, D, window);
   if (s != SWATTN_OK) return s;
-  if (!all_aligned({q, k, v, dO, workspace, dq}) || lse == nullptr) return SWATTN_ERR_INVALID_ARG;
-  return hip_status(swattn::launch_bwd_dq(bf16, q, k, v, dO, lse, (const float *)workspace, dq, B,
+  if (!all_aligned({q, k, v, o, dO, workspace, dq}) || lse == nullptr)
+    return SWATTN_ERR_INVALID_ARG;
+  return hip_status(swattn::launch_bwd_dq(bf16, q, k, v, o, dO, lse, (float *)workspace, dq, B,
                                           H, T, D, window, scale, st));
 }
 
@@ -201,17 +206,17 @@ int swattn_bwd_dkdv_f32(const float *q, const float *k, const float *v, const fl
                   (hipStream_t)stream);
 }
 
-int swattn_bwd_dq(const void *q, const void *k, const void *v, const void *dO, const float *lse,
-                  const void *workspace, void *dq, int B, int H, int T, int D, int window,
-                  float scale, swattn_stream_t stream) {
-  return bwd_dq(true, q, k, v, dO, lse, workspace, dq, B, H, T, D, window, scale,
+int swattn_bwd_dq(const void *q, const void *k, const void *v, const void *o, const void *dO,
+                  const float *lse, void *workspace, void *dq, int B, int H, int T, int D,
+                  int window, float scale, swattn_stream_t stream) {
+  return bwd_dq(true, q, k, v, o, dO, lse, workspace, dq, B, H, T, D, window, scale,
                 (hipStream_t)stream);
 }
 
-int swattn_bwd_dq_f32(const float *q, const float *k, const float *v, const float *dO,
-                      const float *lse, const void *workspace, float *dq, int B, int H, int T,
-                      int D, int window, float scale, swattn_stream_t stream) {
-  return bwd_dq(false, q, k, v, dO, lse, workspace, dq, B, H, T, D, window, scale,
+int swattn_bwd_dq_f32(const float *q, const float *k, const float *v, const float *o,
+                      const float *dO, const float *lse, void *workspace, float *dq, int B, int H,
+                      int T, int D, int window, float scale, swattn_stream_t stream) {
+  return bwd_dq(false, q, k, v, o, dO, lse, workspace, dq, B, H, T, D, window, scale,
                 (hipStream_t)stream);
 }
 

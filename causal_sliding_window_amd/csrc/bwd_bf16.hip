@@ -4,7 +4,7 @@
 // Gradients of L = sum_i dO_i . o_i for the attention of the nanochat guide's
 // section 5 (the training step back-propagates through it).  With P recomputed
 // from the stored LSE:
-//   delta_i = dO_i . o_i                       (bwd_pre kernel)
+//   delta_i = dO_i . o_i                       (bwd_pre kernel, or the dq kernel itself)
 //   dV = P^T dO,  dK = scale * dS^T Q           (dkdv kernel, one pass per key block)
 //   dQ = scale * dS K                           (dq kernel, one pass per query block)
 //   with dP = dO V^T and dS = P * (dP - delta).
@@ -13,6 +13,9 @@
 //
 // Inside the dQ pass S^T = K Q^T is formed with one query per lane (as in the
 // forward) and dS^T feeds dQ^T = K^T dS^T; K^T comes from transposed LDS reads.
+// The dQ pass computes delta for its own queries from o and dO (rows it reads
+// anyway) and writes it to the workspace, so in the full backward it runs first
+// and the dK/dV pass reads delta from there: no separate preprocess launch.
 #include <type_traits>
 
 #include "common.h"
@@ -61,9 +64,9 @@ struct DqCfg {
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, const uint16_t *__restrict__ dO,
-    const float *__restrict__ lse, const float *__restrict__ delta, uint16_t *__restrict__ dq,
-    int B, int H, int T, int window, float scale, int nqt) {
+    const uint16_t *__restrict__ v, const uint16_t *__restrict__ o,
+    const uint16_t *__restrict__ dO, const float *__restrict__ lse, float *__restrict__ delta,
+    uint16_t *__restrict__ dq, int B, int H, int T, int window, float scale, int nqt) {
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * C::TSZ];  // [buf][K, V]
 
@@ -101,7 +104,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     }
   }
   const float l2 = my_q < T ? lse[(size_t)bh * T + my_q] * kLog2e : INFINITY;
-  const float dl = my_q < T ? delta[(size_t)bh * T + my_q] : 0.f;
+  // delta = dO . o of the lane's query (each half of the wave holds half of the
+  // row), also published in the workspace for the dK/dV pass
+  float dl;
+  {
+    const int row = min(my_q, T - 1);
+    float part = 0.f;
+#pragma unroll
+    for (int st = 0; st < C::KST; ++st) {
+      const u32x4 ov = *reinterpret_cast<const u32x4 *>(o + base + (size_t)row * rs + 16 * st + 8 * h);
+      const u32x4 gv = __builtin_bit_cast(u32x4, gr[st]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        part += bf16_lo(ov[e]) * bf16_lo(gv[e]) + bf16_hi(ov[e]) * bf16_hi(gv[e]);
+    }
+    dl = xhalf_sum(part);
+    if (my_q < T && h == 0) delta[(size_t)bh * T + my_q] = dl;
+  }
   const float c = scale * kLog2e;
 
   f32x16 acc[C::NDB];
@@ -212,19 +231,19 @@ hipError_t launch_bwd_pre_bf16(const void *o, const void *dO, float *delta, int 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq_bf16(const void *q, const void *k, const void *v, const void *dO,
-                              const float *lse, const float *delta, void *dq, int B, int H,
-                              int T, int D, int window, float scale, hipStream_t st) {
+hipError_t launch_bwd_dq_bf16(const void *q, const void *k, const void *v, const void *o,
+                              const void *dO, const float *lse, float *delta, void *dq, int B,
+                              int H, int T, int D, int window, float scale, hipStream_t st) {
   const int nqt = (T + 127) / 128;
   const unsigned nb = (unsigned)(nqt * B * H);
   if (D == 128)
     bwd_dq_bf16_kernel<128><<<nb, 256, 0, st>>>(
-        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dO, lse,
-        delta, (uint16_t *)dq, B, H, T, window, scale, nqt);
+        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)o,
+        (const uint16_t *)dO, lse, delta, (uint16_t *)dq, B, H, T, window, scale, nqt);
   else
     bwd_dq_bf16_kernel<64><<<nb, 256, 0, st>>>(
-        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dO, lse,
-        delta, (uint16_t *)dq, B, H, T, window, scale, nqt);
+        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)o,
+        (const uint16_t *)dO, lse, delta, (uint16_t *)dq, B, H, T, window, scale, nqt);
   return hipGetLastError();
 }
 

@@ -23,18 +23,19 @@ hipError_t launch_bwd_dkdv(bool bf16, const void *q, const void *k, const void *
                            const void *dO, const float *lse, const float *delta, void *dk,
                            void *dv, int B, int H, int T, int D, int window, float scale,
                            hipStream_t st);
-hipError_t launch_bwd_dq(bool bf16, const void *q, const void *k, const void *v, const void *dO,
-                         const float *lse, const float *delta, void *dq, int B, int H, int T,
-                         int D, int window, float scale, hipStream_t st);
+// dQ pass; also computes delta = rowsum(dO * o) and writes it to `delta`.
+hipError_t launch_bwd_dq(bool bf16, const void *q, const void *k, const void *v, const void *o,
+                         const void *dO, const float *lse, float *delta, void *dq, int B, int H,
+                         int T, int D, int window, float scale, hipStream_t st);
 
 hipError_t launch_bwd_pre_bf16(const void *o, const void *dO, float *delta, int B, int H, int T,
                                int D, hipStream_t st);
 hipError_t launch_bwd_dkdv_bf16(const void *q, const void *k, const void *v, const void *dO,
                                 const float *lse, const float *delta, void *dk, void *dv, int B,
                                 int H, int T, int D, int window, float scale, hipStream_t st);
-hipError_t launch_bwd_dq_bf16(const void *q, const void *k, const void *v, const void *dO,
-                              const float *lse, const float *delta, void *dq, int B, int H,
-                              int T, int D, int window, float scale, hipStream_t st);
+hipError_t launch_bwd_dq_bf16(const void *q, const void *k, const void *v, const void *o,
+                              const void *dO, const float *lse, float *delta, void *dq, int B,
+                              int H, int T, int D, int window, float scale, hipStream_t st);
 hipError_t launch_bwd_pre_f32(const float *o, const float *dO, float *delta, int B, int H, int T,
                               int D, hipStream_t st);
 hipError_t launch_bwd_dkdv_f32(const float *q, const float *k, const float *v, const float *dO,

@@ -39,8 +39,8 @@ _SIGS = {
     "swattn_bwd_preprocess_f32": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
     "swattn_bwd_dkdv": ([_P] * 8 + [_I] * 5 + [_F, _P], _I),
     "swattn_bwd_dkdv_f32": ([_P] * 8 + [_I] * 5 + [_F, _P], _I),
-    "swattn_bwd_dq": ([_P] * 7 + [_I] * 5 + [_F, _P], _I),
-    "swattn_bwd_dq_f32": ([_P] * 7 + [_I] * 5 + [_F, _P], _I),
+    "swattn_bwd_dq": ([_P] * 8 + [_I] * 5 + [_F, _P], _I),
+    "swattn_bwd_dq_f32": ([_P] * 8 + [_I] * 5 + [_F, _P], _I),
     "swattn_decode_workspace_size": ([_I] * 5, ctypes.c_size_t),
     "swattn_decode": ([_P] * 6 + [_I] * 5 + [_F, _P, _P], _I),
     "swattn_decode_f32": ([_P] * 6 + [_I] * 5 + [_F, _P, _P], _I),
@@ -160,7 +160,7 @@ def _bwd_stage_checks(q, tensors, lse, workspace):
 
 
 def swattn_bwd_preprocess(o, do, workspace, stream=None):
-    """delta = rowsum(dO * o) into the workspace (first backward pass)."""
+    """delta = rowsum(dO * o) into the workspace (only needed to run dK/dV before dQ)."""
     B, T, H, D = _bwd_stage_checks(o, (("o", o), ("do", do)), None, workspace)
     fn = getattr(lib(), "swattn_bwd_preprocess" + _kind(o.dtype))
     _check(fn(_ptr(o), _ptr(do), _ptr(workspace), B, H, T, D, _stream(stream, o.device)),
@@ -168,7 +168,8 @@ def swattn_bwd_preprocess(o, do, workspace, stream=None):
 
 
 def swattn_bwd_dkdv(q, k, v, do, lse, workspace, dk, dv, window: int, scale: float, stream=None):
-    """dK, dV pass (needs the preprocess's workspace)."""
+    """dK, dV pass; reads delta from the workspace (written by swattn_bwd_dq or the
+    preprocess)."""
     B, T, H, D = _bwd_stage_checks(q, (("q", q), ("k", k), ("v", v), ("do", do), ("dk", dk),
                                        ("dv", dv)), lse, workspace)
     fn = getattr(lib(), "swattn_bwd_dkdv" + _kind(q.dtype))
@@ -176,13 +177,13 @@ def swattn_bwd_dkdv(q, k, v, do, lse, workspace, dk, dv, window: int, scale: flo
               B, H, T, D, int(window), float(scale), _stream(stream, q.device)), "swattn_bwd_dkdv")
 
 
-def swattn_bwd_dq(q, k, v, do, lse, workspace, dq, window: int, scale: float, stream=None):
-    """dQ pass (needs the preprocess's workspace)."""
-    B, T, H, D = _bwd_stage_checks(q, (("q", q), ("k", k), ("v", v), ("do", do), ("dq", dq)),
-                                   lse, workspace)
+def swattn_bwd_dq(q, k, v, o, do, lse, workspace, dq, window: int, scale: float, stream=None):
+    """dQ pass; also writes delta = rowsum(dO * o) into the workspace."""
+    B, T, H, D = _bwd_stage_checks(q, (("q", q), ("k", k), ("v", v), ("o", o), ("do", do),
+                                       ("dq", dq)), lse, workspace)
     fn = getattr(lib(), "swattn_bwd_dq" + _kind(q.dtype))
-    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(workspace), _ptr(dq), B, H, T,
-              D, int(window), float(scale), _stream(stream, q.device)), "swattn_bwd_dq")
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(workspace), _ptr(dq),
+              B, H, T, D, int(window), float(scale), _stream(stream, q.device)), "swattn_bwd_dq")
 
 
 swattn_bwd_preprocess_f32 = swattn_bwd_preprocess

@@ -111,11 +111,14 @@ int swattn_bwd_f32(const float *q, const float *k, const float *v,
                    float scale, void *workspace, swattn_stream_t stream);
 
 /*
- * The three passes of swattn_bwd, callable on their own (to time them, or to run
- * the two independent gradient passes on different streams).  swattn_bwd is
- * exactly: swattn_bwd_preprocess (delta = rowsum(dO * o) into the workspace), then
- * swattn_bwd_dkdv and swattn_bwd_dq, which both read that workspace and may run in
- * either order or concurrently once the preprocess has finished.
+ * The passes of swattn_bwd, callable on their own (to time them, or to overlap
+ * them with other work).  swattn_bwd is exactly swattn_bwd_dq followed by
+ * swattn_bwd_dkdv on the same workspace:
+ *   swattn_bwd_dq          dQ; it also computes delta = rowsum(dO * o) (fp32, per
+ *                          query) and writes it to the workspace;
+ *   swattn_bwd_dkdv        dK, dV; reads delta from the workspace, so it must run
+ *                          after swattn_bwd_dq or swattn_bwd_preprocess;
+ *   swattn_bwd_preprocess  delta alone (for running dK/dV before or beside dQ).
  */
 int swattn_bwd_preprocess(const void *o, const void *dO, void *workspace, int B, int H,
                           int T, int D, swattn_stream_t stream);
@@ -129,12 +132,12 @@ int swattn_bwd_dkdv_f32(const float *q, const float *k, const float *v,
                         const float *dO, const float *lse, const void *workspace,
                         float *dk, float *dv, int B, int H, int T, int D, int window,
                         float scale, swattn_stream_t stream);
-int swattn_bwd_dq(const void *q, const void *k, const void *v, const void *dO,
-                  const float *lse, const void *workspace, void *dq, int B, int H, int T,
-                  int D, int window, float scale, swattn_stream_t stream);
-int swattn_bwd_dq_f32(const float *q, const float *k, const float *v, const float *dO,
-                      const float *lse, const void *workspace, float *dq, int B, int H,
-                      int T, int D, int window, float scale, swattn_stream_t stream);
+int swattn_bwd_dq(const void *q, const void *k, const void *v, const void *o,
+                  const void *dO, const float *lse, void *workspace, void *dq, int B, int H,
+                  int T, int D, int window, float scale, swattn_stream_t stream);
+int swattn_bwd_dq_f32(const float *q, const float *k, const float *v, const float *o,
+                      const float *dO, const float *lse, void *workspace, float *dq, int B,
+                      int H, int T, int D, int window, float scale, swattn_stream_t stream);
 
 /*
  * Decode workspace in bytes: per (sequence, head, KV split) one float32 partial

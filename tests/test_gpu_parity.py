@@ -264,6 +264,41 @@ def test_runs_on_a_side_stream():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_stages(dtype):
+    """swattn_bwd is exactly swattn_bwd_dq then swattn_bwd_dkdv on one workspace
+    (bitwise); the dQ pass leaves delta = rowsum(dO * o) in the workspace, equal to
+    the preprocess's up to summation order; dK/dV fed the preprocess's delta agrees."""
+    D = 64 if dtype == "f32" else 128
+    x = inputs.training_inputs(2, 300, 3, D, dtype, seed=5, qk_norm=True)
+    g = _gpu(x)
+    W, sc = 100, 1.0 / math.sqrt(D)
+    o, lse = swattn.fwd(g["q"], g["k"], g["v"], W, sc)
+    ref = swattn.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, W, sc)
+    B, T, H, _ = g["q"].shape
+    ws = torch.zeros(swattn.swattn_bwd_workspace_size(B, H, T, D), dtype=torch.uint8, device=DEV)
+    dq, dk, dv = (torch.empty_like(g["q"]) for _ in range(3))
+    swattn.swattn_bwd_dq(g["q"], g["k"], g["v"], o, g["do"], lse, ws, dq, W, sc)
+    swattn.swattn_bwd_dkdv(g["q"], g["k"], g["v"], g["do"], lse, ws, dk, dv, W, sc)
+    torch.cuda.synchronize()
+    for a, b in zip((dq, dk, dv), ref):
+        assert torch.equal(a, b)
+    delta_dq = ws.view(torch.float32)[: B * H * T].clone()
+    ws2 = torch.zeros_like(ws)
+    swattn.swattn_bwd_preprocess(o, g["do"], ws2)
+    dk2, dv2 = torch.empty_like(dk), torch.empty_like(dv)
+    swattn.swattn_bwd_dkdv(g["q"], g["k"], g["v"], g["do"], lse, ws2, dk2, dv2, W, sc)
+    torch.cuda.synchronize()
+    delta_pre = ws2.view(torch.float32)[: B * H * T]
+    ref_delta = (o.double() * g["do"].double()).sum(-1).permute(0, 2, 1).reshape(-1)
+    tol = 1e-4 * (1 + ref_delta.abs())
+    assert torch.all((delta_dq.double() - ref_delta).abs() <= tol)
+    assert torch.all((delta_pre.double() - ref_delta).abs() <= tol)
+    bar = 1e-5 if dtype == "f32" else 2e-2
+    assert (dk2.double() - dk.double()).abs().max().item() <= bar
+    assert (dv2.double() - dv.double()).abs().max().item() <= bar
+
+
 def test_w1_gradients_vanish():
     """W = 1: o = v and dv = dO after bf16 rounding; dq and dk vanish."""
     x = inputs.training_inputs(1, 130, 2, 128, "bf16", seed=5, qk_norm=True)
