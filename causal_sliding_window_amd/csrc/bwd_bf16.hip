@@ -54,11 +54,14 @@ __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(const uint16_t *__res
 template <int D>
 struct DqCfg {
   static constexpr int BM = 128;          // queries per workgroup (4 waves x 32)
-  static constexpr int BN = 64;           // keys per LDS tile
-  static constexpr int TSZ = BN * D;
+  static constexpr int BN = 32;           // keys per tile
+  static constexpr int NSLOT = 3;         // LDS tile slots (tile t in slot t % 3)
+  static constexpr int TSZ = BN * D;      // elements of one K (or V) tile
   static constexpr int NDB = D / 32;
   static constexpr int KST = D / 16;
-  static constexpr int CPW = (2 * TSZ * 2 / 1024) / 4;
+  static constexpr int HALF = TSZ * 2 / 1024;  // 1-KB pieces of one tensor's tile
+  static constexpr int CPW = 2 * HALF / 4;     // pieces per wave and tile (K and V)
+  static constexpr int RG = BN / 16;           // 16-row groups per 32-column block
 };
 
 template <int D>
@@ -68,11 +71,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const uint16_t *__restrict__ dO, const float *__restrict__ lse, float *__restrict__ delta,
     uint16_t *__restrict__ dq, int B, int H, int T, int window, float scale, int nqt) {
   using C = DqCfg<D>;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * C::TSZ];  // [buf][K, V]
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[C::NSLOT * 2 * C::TSZ];  // [slot][K, V]
 
   const int BH = B * H;
   const int bid = blockIdx.x;
-  const int qt = nqt - 1 - bid / BH;
+  const int qt = nqt - 1 - bid / BH;  // longest (latest) query blocks first
   const int bh = bid % BH;
   const int b = bh / H, hh = bh % H;
   const int q0 = qt * C::BM;
@@ -86,33 +89,40 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const int qw0 = q0 + 32 * w;
   const int my_q = qw0 + ln;
 
+  // key tiles of the workgroup and of this wave
   const int q_last = min(T, q0 + C::BM) - 1;
   const int k_lo = window > 0 ? max(0, q0 - window + 1) : 0;
   const int kt0 = k_lo / C::BN, kt1 = q_last / C::BN;
-  const int wq_lo = qw0, wq_hi = min(T - 1, qw0 + 31);
-  const int wk_lo = window > 0 ? wq_lo - window + 1 : 0;
+  int wkt0 = 1 << 30, wkt1 = -1;
+  if (qw0 < T) {
+    wkt0 = (window > 0 ? max(0, qw0 - window + 1) : 0) / C::BN;
+    wkt1 = min(T - 1, qw0 + 31) / C::BN;
+  }
+  const int wq_hi = min(T - 1, qw0 + 31);
   // key kk is visible to my_q iff 0 <= my_q - kk <= wm1
   const unsigned wm1 = window > 0 ? (unsigned)(window - 1) : 0x7fffffffu;
 
+  // Q and dO rows of the lane's query (B operands), rows past T read as zero
   bf16x8 qr[C::KST], gr[C::KST];
-  {
-    const int row = min(my_q, T - 1);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (uint32_t)T * rs * 2);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(gb, (uint32_t)T * rs * 2);
 #pragma unroll
-    for (int st = 0; st < C::KST; ++st) {
-      qr[st] = *reinterpret_cast<const bf16x8 *>(qb + (size_t)row * rs + 16 * st + 8 * h);
-      gr[st] = *reinterpret_cast<const bf16x8 *>(gb + (size_t)row * rs + 16 * st + 8 * h);
-    }
+  for (int st = 0; st < C::KST; ++st) {
+    const uint32_t off = (my_q * rs + 16 * st + 8 * h) * 2;
+    qr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+    gr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
   }
   const float l2 = my_q < T ? lse[(size_t)bh * T + my_q] * kLog2e : INFINITY;
   // delta = dO . o of the lane's query (each half of the wave holds half of the
   // row), also published in the workspace for the dK/dV pass
   float dl;
   {
-    const int row = min(my_q, T - 1);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + base, (uint32_t)T * rs * 2);
     float part = 0.f;
 #pragma unroll
     for (int st = 0; st < C::KST; ++st) {
-      const u32x4 ov = *reinterpret_cast<const u32x4 *>(o + base + (size_t)row * rs + 16 * st + 8 * h);
+      const u32x4 ov =
+          __builtin_amdgcn_raw_buffer_load_b128(ro, (my_q * rs + 16 * st + 8 * h) * 2, 0, 0);
       const u32x4 gv = __builtin_bit_cast(u32x4, gr[st]);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -128,91 +138,164 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   for (int d = 0; d < C::NDB; ++d) acc[d] = f32x16{};
 
   // K and V tiles (rows in swap23 order, d-block-major; rows past T read as zero
-  // and are masked) by buffer -> LDS copies.  Piece j (1 KB): tensor j / (4 NDB),
-  // LDS block db = (j % (4 NDB)) / 4, rows 16 (j % 4) .. + 15.
+  // and are masked) by buffer -> LDS copies.  Piece j (1 KB): tensor j / HALF, LDS
+  // block db = (j % HALF) / RG, rows 16 ((j % HALF) % RG) .. + 15.
   const int rl = lane >> 2;
   const int lc = (lane & 3) ^ ((lane >> 4) & 3);  // logical chunk stored at this position
   const uint32_t lane_off = (swap23(rl) * rs + 8 * lc) * 2;
-  auto issue_tile = [&](int kt, int buf) {
+  auto issue = [&](int kt) {
+    const int slot = kt % C::NSLOT;
     const int row0 = kt * C::BN;
     const uint32_t nbytes = (uint32_t)(T - row0) * rs * 2;
 #pragma unroll
     for (int cc = 0; cc < C::CPW; ++cc) {
       const int j = w * C::CPW + cc;
-      const int tensor = j / (4 * C::NDB), jj = j % (4 * C::NDB);
-      const int db = jj >> 2, row16 = 16 * (jj & 3);
+      const int tensor = j / C::HALF, jj = j % C::HALF;
+      const int db = jj / C::RG, row16 = 16 * (jj % C::RG);
       const __amdgpu_buffer_rsrc_t r = make_rsrc((tensor ? vb : kb) + (size_t)row0 * rs, nbytes);
-      buf_copy16_to_lds(r, smem + (2 * buf + tensor) * C::TSZ + db * (C::BN * 32) + row16 * 32,
+      buf_copy16_to_lds(r, smem + (2 * slot + tensor) * C::TSZ + db * (C::BN * 32) + row16 * 32,
                         lane_off + (row16 * rs + 32 * db) * 2);
     }
   };
+  auto k_tile = [&](int kt) { return smem + 2 * (kt % C::NSLOT) * C::TSZ; };
 
-  issue_tile(kt0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const int buf = (kt - kt0) & 1;
-    if (kt < kt1) issue_tile(kt + 1, buf ^ 1);
-    const int kbase = kt * C::BN;
-    const bool active = wq_hi >= wq_lo && kbase <= wq_hi && kbase + C::BN - 1 >= wk_lo;
-    if (active) {
-      const bool need_mask =
-          (kbase + C::BN - 1 > wq_lo) || (window > 0 && wq_hi - kbase >= window);
-      const uint16_t *Kt = smem + 2 * buf * C::TSZ;
-      const uint16_t *Vt = Kt + C::TSZ;
-      const int rel0 = my_q - kbase - 8 * h;
+  // S^T = K Q^T and dP^T = V dO^T of a tile, one query per lane: register i of half
+  // h holds key c_row(i, h) of the tile.
+  auto sdp = [&](int kt, f32x16 &s, f32x16 &dp) {
+    const uint16_t *Kt = k_tile(kt), *Vt = Kt + C::TSZ;
+    bf16x8 ka[C::KST], va[C::KST];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
-        const int row = sb * 32 + ln;
-        bf16x8 ka[C::KST], va[C::KST];
-#pragma unroll
-        for (int st = 0; st < C::KST; ++st) {
-          ka[st] = lds_read_b128(Kt + dt_off<C::BN>(row, 2 * st + h));
-          va[st] = lds_read_b128(Vt + dt_off<C::BN>(row, 2 * st + h));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int st = 0; st < C::KST; ++st) {
-          s = mfma32(ka[st], qr[st], s);
-          dp = mfma32(va[st], gr[st], dp);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(fmaf(s[i], c, -l2));
-          // register i holds key kbase + sb*32 + c_row(i, h) = kbase + 8h + sb*32 + c_row(i, 0)
-          if (need_mask) p = (unsigned)(rel0 - sb * 32 - c_row(i, 0)) <= wm1 ? p : 0.f;
-          s[i] = p * (dp[i] - dl);
-        }
-        // K^T operands: one asm block, so the copies of the next tile stay in flight
-        bf16x8 kt_op[2][C::NDB];
-        dt_read_tr_perm_block<C::BN, C::NDB>(Kt, sb * 32, lane, kt_op);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 dsb = to_bf16x8(s, 8 * t);
-#pragma unroll
-          for (int d = 0; d < C::NDB; ++d) acc[d] = mfma32(kt_op[t][d], dsb, acc[d]);
-        }
-      }
+    for (int st = 0; st < C::KST; ++st) {
+      ka[st] = lds_read_b128(Kt + dt_off<C::BN>(ln, 2 * st + h));
+      va[st] = lds_read_b128(Vt + dt_off<C::BN>(ln, 2 * st + h));
     }
+#pragma unroll
+    for (int st = 0; st < C::KST; ++st) {
+      s = mfma32(ka[st], qr[st], st ? s : f32x16{});
+      dp = mfma32(va[st], gr[st], st ? dp : f32x16{});
+    }
+  };
+
+  // dS = P (dP - delta) for elements [e0, e0 + n) of a tile (into dp).
+  auto ds_elems = [&](auto mask_tag, f32x16 &s, f32x16 &dp, int rel0, int e0, int n) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+    for (int i = e0; i < e0 + n; ++i) {
+      float p = fast_exp2(fmaf(s[i], c, -l2));
+      if (MASK) p = (unsigned)(rel0 - c_row(i, 0)) <= wm1 ? p : 0.f;
+      dp[i] = p * (dp[i] - dl);
+    }
+  };
+  // dQ^T += K^T dS^T for a tile (K^T by one asm block of transposed reads, so the
+  // copies in flight are not waited for)
+  auto dq_mfma = [&](int kt, const f32x16 &ds) {
+    bf16x8 kt_op[2][C::NDB];
+    dt_read_tr_perm_block<C::BN, C::NDB>(k_tile(kt), 0, lane, kt_op);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 dsb = to_bf16x8(ds, 8 * t);
+#pragma unroll
+      for (int d = 0; d < C::NDB; ++d) acc[d] = mfma32(kt_op[t][d], dsb, acc[d]);
+    }
+  };
+  auto pin = [](float x) {
+    asm volatile("" ::"v"(x));
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // One pipeline step for tile kt (S^T, dP^T in sc, dpc): the copies of tile kt + 2
+  // start first; the S / dP MFMAs of tile kt + 1 are issued one pair at a time
+  // between the slices of tile kt's dS work, then dQ += dS K for tile kt.
+  auto step = [&](auto mask_tag, int kt, f32x16 &sc, f32x16 &dpc, f32x16 &sn, f32x16 &dpn) {
+    if (kt + 2 <= kt1) issue(kt + 2);
+    const uint16_t *Kn = k_tile(kt + 1), *Vn = Kn + C::TSZ;
+    // operands are read AHEAD slices before their MFMAs
+    constexpr int AHEAD = 2;
+    bf16x8 ka[C::KST], va[C::KST];
+    auto read_ops = [&](int st) {
+      ka[st] = lds_read_b128(Kn + dt_off<C::BN>(ln, 2 * st + h));
+      va[st] = lds_read_b128(Vn + dt_off<C::BN>(ln, 2 * st + h));
+    };
+#pragma unroll
+    for (int st = 0; st < AHEAD; ++st) read_ops(st);
+    __builtin_amdgcn_sched_barrier(0);
+    const int rel0 = my_q - kt * C::BN - 8 * h;
+    constexpr int EPS = 16 / C::KST;  // elements per slice
+#pragma unroll
+    for (int st = 0; st < C::KST; ++st) {
+      if (st + AHEAD < C::KST) read_ops(st + AHEAD);
+      sn = mfma32(ka[st], qr[st], st ? sn : f32x16{});
+      dpn = mfma32(va[st], gr[st], st ? dpn : f32x16{});
+      __builtin_amdgcn_sched_barrier(0);
+      ds_elems(mask_tag, sc, dpc, rel0, EPS * st, EPS);
+      pin(dpc[EPS * st + EPS - 1]);
+    }
+    dq_mfma(kt, dpc);
+  };
+  auto last_step = [&](int kt, f32x16 &sc, f32x16 &dpc) {
+    if (kt + 2 <= kt1) issue(kt + 2);
+    ds_elems(std::true_type{}, sc, dpc, my_q - kt * C::BN - 8 * h, 0, 16);
+    dq_mfma(kt, dpc);
+  };
+  auto sync = [&] {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+
+  // prologue: tiles kt0 and kt0 + 1
+  issue(kt0);
+  if (kt0 < kt1) issue(kt0 + 1);
+  sync();
+  f32x16 sc, dpc, sn, dpn;
+  if (wkt0 == kt0) sdp(kt0, sc, dpc);
+
+  // Phases of the wave (one barrier per tile of the workgroup in each): idle tiles,
+  // S / dP of its first tile, tiles crossing the window's lower edge (masked),
+  // unmasked tiles, its diagonal tile (masked, no S / dP ahead), idle tiles.
+  const int mlim = (window > 0 && wq_hi - window >= 0) ? (wq_hi - window) / C::BN + 1 : 0;
+  int kt = kt0;
+  for (; kt < min(wkt0 - 1, kt1 + 1); ++kt) {
+    if (kt + 2 <= kt1) issue(kt + 2);
+    sync();
+  }
+  if (wkt0 > kt0 && kt == wkt0 - 1) {
+    if (kt + 2 <= kt1) issue(kt + 2);
+    sdp(kt + 1, sc, dpc);
+    sync();
+    ++kt;
+  }
+  for (; kt < min(wkt1, mlim); ++kt) {
+    step(std::true_type{}, kt, sc, dpc, sn, dpn);
+    sc = sn;
+    dpc = dpn;
+    sync();
+  }
+  for (; kt < wkt1; ++kt) {
+    step(std::false_type{}, kt, sc, dpc, sn, dpn);
+    sc = sn;
+    dpc = dpn;
+    sync();
+  }
+  if (kt == wkt1) {
+    last_step(kt, sc, dpc);
+    sync();
+    ++kt;
+  }
+  for (; kt <= kt1; ++kt) {
+    if (kt + 2 <= kt1) issue(kt + 2);
+    sync();
   }
 
   if (my_q < T) {
-    uint16_t *dqb = dq + base;
+    uint16_t *dqr = dq + base + (size_t)my_q * rs;
 #pragma unroll
     for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        u32x2 pk;
-        pk[0] = (uint32_t)f32_to_bf16_bits(acc[d][4 * g] * scale) |
-                ((uint32_t)f32_to_bf16_bits(acc[d][4 * g + 1] * scale) << 16);
-        pk[1] = (uint32_t)f32_to_bf16_bits(acc[d][4 * g + 2] * scale) |
-                ((uint32_t)f32_to_bf16_bits(acc[d][4 * g + 3] * scale) << 16);
-        *reinterpret_cast<u32x2 *>(dqb + (size_t)my_q * rs + 32 * d + 8 * g + 4 * h) = pk;
+        bf16x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[d][4 * g + e] * scale);
+        *reinterpret_cast<bf16x4 *>(dqr + 32 * d + 8 * g + 4 * h) = pk;
       }
   }
 }
