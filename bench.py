@@ -253,8 +253,16 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
 
     fe, wr = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
     pick = lambda d, key: next((v for k, v in d.items() if key in k), None)  # noqa: E731
-    copy_f = pick(fe, "copy") or pick(fe, "elementwise")
-    copy_w = pick(wr, "copy") or pick(wr, "elementwise")
+
+    def copy_reading(path, counter):
+        # the calibration copy is the largest copy dispatch (the runtime issues small
+        # copies of its own)
+        vals = [float(r["Counter_Value"]) * 1024.0 for r in csv.DictReader(open(path))
+                if r.get("Counter_Name") == counter and "copy" in r["Kernel_Name"]]
+        return max(vals) if vals else None
+
+    copy_f = copy_reading(fetch_csv, "FETCH_SIZE")
+    copy_w = copy_reading(write_csv, "WRITE_SIZE")
     names = {"fwd": "fwd_bf16_kernel",
              "bwd_dkdv": "bwd_dkdv_bf16_kernel", "bwd_dq": "bwd_dq_bf16_kernel",
              "decode_split": "decode_split_kernel"}
