@@ -142,6 +142,18 @@ __device__ __forceinline__ bf16x8 dt_read_tr(const uint16_t *tile, int row0, int
              lds_read_tr(sub + r2 * 32 + 8 * (lc ^ ((r2 >> 2) & 3)) + w));
 }
 
+// Workgroup barrier for handing LDS tiles between waves.  The caller first waits
+// (s_waitcnt) for what must be complete: its own copies into the tiles about to be
+// read (vmcnt) and its own LDS reads of the tiles about to be overwritten
+// (lgkmcnt).  Unlike __syncthreads() there is no memory fence, whose
+// s_waitcnt vmcnt(0) would also wait for the copies prefetching later tiles.  The
+// empty asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;

@@ -8,9 +8,10 @@
 // rows in registers as MFMA B operands; S = Q K^T and dP = dO V^T are formed with
 // one key per lane, so P and dS feed dV^T = dO^T P and dK^T = Q^T dS as B
 // operands straight from registers; dO^T and Q^T come from transposed LDS reads.
-// Query tiles of 32 rows reach LDS by direct buffer -> LDS copies (three slots,
-// issued two tiles ahead); each step overlaps the S / dP MFMAs of the next tile
-// with the gradient-side ALU work of the current one.
+// Query tiles of 32 rows reach LDS by direct buffer -> LDS copies (four slots,
+// issued three tiles ahead, each step waiting only for the tile it needs next);
+// each step overlaps the S / dP MFMAs of the next tile with the gradient-side ALU
+// work of the current one.
 //
 // Built without -amdgpu-mfma-vgpr-form: the dK / dV accumulators stay in AGPRs,
 // which leaves the arch VGPRs to the operands.
@@ -26,14 +27,21 @@ template <int D>
 struct DkdvCfg {
   static constexpr int BK = 128;          // keys per workgroup (4 waves x 32)
   static constexpr int BQ = 32;           // queries per tile
-  static constexpr int NSLOT = 3;         // LDS tile slots (tile t in slot t % 3)
+  static constexpr int NSLOT = 4;         // LDS tile slots (tile t in slot t % 4)
+  static constexpr int AHEAD = NSLOT - 1; // tiles are copied this many steps ahead
   static constexpr int TSZ = BQ * D;      // elements of one Q (or dO) tile
   static constexpr int NDB = D / 32;
   static constexpr int KST = D / 16;
   static constexpr int HALF = TSZ * 2 / 1024;  // 1-KB pieces of one tensor's tile
   static constexpr int CPW = 2 * HALF / 4;     // pieces per wave and tile (Q and dO)
   static constexpr int RG = BQ / 16;           // 16-row groups per 32-column block
+  static constexpr int NCOPY = CPW + 1;        // copies per wave and tile (+ lse/delta)
 };
+
+// s_waitcnt immediate: at most N vector-memory operations of the wave in flight,
+// all LDS operations done, exports not waited for.
+template <int N>
+constexpr int kWaitVm = (N & 15) | ((N >> 4) << 14) | (7 << 4);
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
@@ -42,9 +50,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     const float *__restrict__ lse, const float *__restrict__ delta, uint16_t *__restrict__ dk,
     uint16_t *__restrict__ dv, int B, int H, int T, int window, float scale, int nkt) {
   using C = DkdvCfg<D>;
-  // [slot][Q, dO][TSZ]; [slot][lse, delta][64]
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[C::NSLOT * 2 * C::TSZ];
-  __shared__ __attribute__((aligned(256))) float vec[C::NSLOT * 2 * 64];
+  // One LDS array (with a single __shared__ variable the compiler keeps the restrict
+  // scopes below): [slot][Q, dO][TSZ] bf16, then [slot][lse, delta, spare, spare][64]
+  // float.
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[C::NSLOT * 2 * C::TSZ +
+                                                          C::NSLOT * 4 * 64 * 2];
+  float *const vec = reinterpret_cast<float *>(smem + C::NSLOT * 2 * C::TSZ);
 
   const int BH = B * H;
   const int bid = blockIdx.x;
@@ -89,6 +100,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       kr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
       vr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
+    // landed before any tile copy is issued: later waits then only count copies
+    __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+    __builtin_amdgcn_sched_barrier(0);
   }
   f32x16 dka[C::NDB], dva[C::NDB];
 #pragma unroll
@@ -105,8 +119,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   const int rl = lane >> 2;
   const int lc = (lane & 3) ^ ((lane >> 4) & 3);  // logical chunk stored at this position
   const uint32_t lane_off = (swap23(rl) * rs + 8 * lc) * 2;
-  auto issue = [&](int qt) {
-    const int slot = qt % C::NSLOT;
+  auto issue_to = [&](int qt, uint16_t *tile, float *vdst) {
     const int row0 = qt * C::BQ;
     const uint32_t nbytes = (uint32_t)(T - row0) * rs * 2;
 #pragma unroll
@@ -115,19 +128,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       const int tensor = j / C::HALF, jj = j % C::HALF;
       const int db = jj / C::RG, row16 = 16 * (jj % C::RG);
       const __amdgpu_buffer_rsrc_t r = make_rsrc((tensor ? gb : qb) + (size_t)row0 * rs, nbytes);
-      buf_copy16_to_lds(r, smem + (2 * slot + tensor) * C::TSZ + db * (C::BQ * 32) + row16 * 32,
+      buf_copy16_to_lds(r, tile + tensor * C::TSZ + db * (C::BQ * 32) + row16 * 32,
                         lane_off + (row16 * rs + 32 * db) * 2);
     }
-    if (w < 2) {
-      const __amdgpu_buffer_rsrc_t r =
-          make_rsrc((w ? delb : lseb) + row0, (uint32_t)(T - row0) * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void *)(vec + (2 * slot + w) * 64), 4, lane * 4,
-          0, 0, 0);
-    }
+    // every wave issues exactly NCOPY copies per tile (waves 2 and 3 fill spare
+    // rows), so the end-of-step wait can count them
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(((w & 1) ? delb : lseb) + row0, (uint32_t)(T - row0) * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)(vdst + w * 64), 4, lane * 4, 0, 0, 0);
   };
   auto q_tile = [&](int qt) { return smem + 2 * (qt % C::NSLOT) * C::TSZ; };
-  auto vec_of = [&](int qt) { return vec + 2 * (qt % C::NSLOT) * 64; };
+  auto vec_of = [&](int qt) { return vec + 4 * (qt % C::NSLOT) * 64; };
+  auto issue = [&](int qt) { issue_to(qt, q_tile(qt), vec_of(qt)); };
 
   // S = Q K^T and dP = dO V^T of a tile, one key per lane: register 8t + j of half
   // h holds query 16t + 8h + j of the tile.
@@ -146,10 +159,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     }
   };
 
-  // Transposed operands of dV^T += dO^T P and dK^T += Q^T dS for a tile.
+  // Transposed operands of dV^T += dO^T P and dK^T += Q^T dS for a tile, by the
+  // asm block that waits only for its own LDS reads (copies stay in flight).
   using TOps = bf16x8[2][C::NDB];
-  auto tr_reads = [&](int qt, TOps &gt, TOps &qtr) {
-    const uint16_t *Qt = q_tile(qt), *Gt = Qt + C::TSZ;
+  auto tr_reads = [&](const uint16_t *Qt, TOps &gt, TOps &qtr) {
+    const uint16_t *Gt = Qt + C::TSZ;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -192,8 +206,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       dka[d] = mfma32(qtr[t][d], ds, dka[d]);
     }
   };
-  auto read_vecs = [&](int qt, f32x4 (&L)[4], f32x4 (&Dl)[4]) {
-    const float *vl = vec_of(qt);
+  auto read_vecs = [&](const float *vl, f32x4 (&L)[4], f32x4 (&Dl)[4]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -208,33 +221,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // One pipeline step for tile qt (S, dP in sc, dpc).  LDS reads first: the
-  // operands of tile qt + 1's S / dP MFMAs (needed first), then the transposed
-  // operands of tile qt, all before the copies of tile qt + 2 start (the compiler
-  // makes a transposed read wait for every global -> LDS copy in flight).  The S /
-  // dP MFMAs of tile qt + 1 (when NEXT) are issued one by one between the slices
-  // of the gradient-side ALU work of tile qt, and the dV / dK MFMAs of tile qt
-  // close the step.
-  auto step = [&](auto mask_tag, auto next_tag, int qt, f32x16 &sc, f32x16 &dpc, f32x16 &sn,
-                  f32x16 &dpn) {
+  // One pipeline step for tile qt (S, dP in sc, dpc).  The copies of tile
+  // qt + AHEAD start first; the operands of tile qt + 1's S / dP MFMAs and tile qt's
+  // lse / delta are read; the S / dP MFMAs of tile qt + 1 (when NEXT) are issued
+  // one pair at a time between the slices of the gradient-side ALU work of tile qt;
+  // then tile qt's transposed operands are read and its dV / dK MFMAs close the
+  // step.  The tiles come in as distinct restrict pointers: with that, the compiler
+  // knows the reads do not touch the tiles being copied and does not make them wait
+  // for the copies in flight (the copies a step reads were awaited at the barrier
+  // before it).
+  auto step_body = [&](auto mask_tag, auto next_tag, int qt, f32x16 &sc, f32x16 &dpc,
+                       f32x16 &sn, f32x16 &dpn, const uint16_t *__restrict__ cur,
+                       const uint16_t *__restrict__ nxt, const float *__restrict__ vcur,
+                       uint16_t *__restrict__ dma, float *__restrict__ vdma) {
     constexpr bool NEXT = decltype(next_tag)::value;
+    if (qt + C::AHEAD <= qt1) issue_to(qt + C::AHEAD, dma, vdma);
     const int rel0 = qt * C::BQ + 8 * h - my_k;
     bf16x8 qa[C::KST], ga[C::KST];
     if constexpr (NEXT) {
-      const uint16_t *Qn = q_tile(qt + 1), *Gn = Qn + C::TSZ;
+      const uint16_t *Gn = nxt + C::TSZ;
 #pragma unroll
       for (int st = 0; st < C::KST; ++st) {
-        qa[st] = lds_read_b128(Qn + dt_off<C::BQ>(ln, 2 * st + h));
+        qa[st] = lds_read_b128(nxt + dt_off<C::BQ>(ln, 2 * st + h));
         ga[st] = lds_read_b128(Gn + dt_off<C::BQ>(ln, 2 * st + h));
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    TOps gt, qtr;
-    tr_reads(qt, gt, qtr);
     f32x4 L[4], Dl[4];
-    read_vecs(qt, L, Dl);
-    __builtin_amdgcn_sched_barrier(0);
-    if (qt + 2 <= qt1) issue(qt + 2);
+    read_vecs(vcur, L, Dl);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NEXT) {
       constexpr int EPS = 16 / C::KST;  // elements per slice
@@ -249,6 +262,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     } else {
       grad_elems(mask_tag, sc, dpc, L, Dl, rel0, 0, 16);
     }
+    TOps gt, qtr;
+    tr_reads(cur, gt, qtr);
     bf16x8 ph0, pl0, ds0, ph1, pl1, ds1;
     pack(sc, dpc, 0, ph0, pl0, ds0);
     __builtin_amdgcn_sched_barrier(0);
@@ -256,15 +271,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     pack(sc, dpc, 1, ph1, pl1, ds1);
     grads(gt, qtr, 1, ph1, pl1, ds1);
   };
-  auto sync = [&] {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  auto step = [&](auto mask_tag, auto next_tag, int qt, f32x16 &sc, f32x16 &dpc, f32x16 &sn,
+                  f32x16 &dpn) {
+    step_body(mask_tag, next_tag, qt, sc, dpc, sn, dpn, q_tile(qt), q_tile(qt + 1), vec_of(qt),
+              q_tile(qt + C::AHEAD), vec_of(qt + C::AHEAD));
+  };
+  // End of step qt: the tile needed next (copied a step earlier) must have landed;
+  // the copies this step issued (tile qt + AHEAD) may stay in flight.
+  auto sync = [&](int qt) {
+    if (qt + C::AHEAD <= qt1) __builtin_amdgcn_s_waitcnt(kWaitVm<C::NCOPY>);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+    lds_barrier();
   };
 
-  // prologue: tiles qt0 and qt0 + 1
-  issue(qt0);
-  if (qt0 < qt1) issue(qt0 + 1);
-  sync();
+  // prologue: tiles qt0 .. qt0 + AHEAD - 1; all but the last must have landed
+  for (int t = qt0; t < qt0 + C::AHEAD && t <= qt1; ++t) issue(t);
+  sync(qt0 - 1);
   f32x16 sc, dpc, sn, dpn;
   if (wqt0 == qt0) sdp(qt0, sc, dpc);
 
@@ -274,13 +296,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // workgroup in every phase.
   int qt = qt0;
   for (; qt < min(wqt0 - 1, qt1 + 1); ++qt) {
-    if (qt + 2 <= qt1) issue(qt + 2);
-    sync();
+    if (qt + C::AHEAD <= qt1) issue(qt + C::AHEAD);
+    sync(qt);
   }
   if (wqt0 > qt0 && qt == wqt0 - 1) {
+    if (qt + C::AHEAD <= qt1) issue(qt + C::AHEAD);
     sdp(qt + 1, sc, dpc);
-    if (qt + 2 <= qt1) issue(qt + 2);
-    sync();
+    sync(qt);
     ++qt;
   }
   auto advance = [&] {
@@ -290,27 +312,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   if (qt == wqt0 && qt < wqt1) {  // diagonal tile
     step(std::true_type{}, std::true_type{}, qt, sc, dpc, sn, dpn);
     advance();
-    sync();
+    sync(qt);
     ++qt;
   }
   for (; qt < min(wqt1, mlo); ++qt) {
     step(std::false_type{}, std::true_type{}, qt, sc, dpc, sn, dpn);
     advance();
-    sync();
+    sync(qt);
   }
   for (; qt < wqt1; ++qt) {
     step(std::true_type{}, std::true_type{}, qt, sc, dpc, sn, dpn);
     advance();
-    sync();
+    sync(qt);
   }
   if (qt == wqt1) {
     step(std::true_type{}, std::false_type{}, qt, sc, dpc, sn, dpn);
-    sync();
+    sync(qt);
     ++qt;
   }
   for (; qt <= qt1; ++qt) {
-    if (qt + 2 <= qt1) issue(qt + 2);
-    sync();
+    if (qt + C::AHEAD <= qt1) issue(qt + C::AHEAD);
+    sync(qt);
   }
 
   if (my_k < T) {
