@@ -27,21 +27,22 @@ template <int D>
 struct DkdvCfg {
   static constexpr int BK = 128;          // keys per workgroup (4 waves x 32)
   static constexpr int BQ = 32;           // queries per tile
-  static constexpr int NSLOT = 4;         // LDS tile slots (tile t in slot t % 4)
+  static constexpr int NSLOT = 5;         // LDS tile slots (tile t in slot t % 5)
   static constexpr int AHEAD = NSLOT - 1; // tiles are copied this many steps ahead
   static constexpr int TSZ = BQ * D;      // elements of one Q (or dO) tile
   static constexpr int NDB = D / 32;
-  static constexpr int KST = D / 16;
+  static constexpr int KST = D / 16;      // = 2 * NDB
   static constexpr int HALF = TSZ * 2 / 1024;  // 1-KB pieces of one tensor's tile
   static constexpr int CPW = 2 * HALF / 4;     // pieces per wave and tile (Q and dO)
   static constexpr int RG = BQ / 16;           // 16-row groups per 32-column block
   static constexpr int NCOPY = CPW + 1;        // copies per wave and tile (+ lse/delta)
+  static constexpr int VSZ = 256;              // floats of lse / delta per slot
 };
 
-// s_waitcnt immediate: at most N vector-memory operations of the wave in flight,
-// all LDS operations done, exports not waited for.
+// s_waitcnt immediate: at most N vector-memory operations of the wave in flight;
+// LDS operations and exports not waited for.
 template <int N>
-constexpr int kWaitVm = (N & 15) | ((N >> 4) << 14) | (7 << 4);
+constexpr int kWaitVm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // scopes below): [slot][Q, dO][TSZ] bf16, then [slot][lse, delta, spare, spare][64]
   // float.
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::NSLOT * 2 * C::TSZ +
-                                                          C::NSLOT * 4 * 64 * 2];
+                                                          C::NSLOT * C::VSZ * 2];
   float *const vec = reinterpret_cast<float *>(smem + C::NSLOT * 2 * C::TSZ);
 
   const int BH = B * H;
@@ -139,81 +140,86 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
         r, (__attribute__((address_space(3))) void *)(vdst + w * 64), 4, lane * 4, 0, 0, 0);
   };
   auto q_tile = [&](int qt) { return smem + 2 * (qt % C::NSLOT) * C::TSZ; };
-  auto vec_of = [&](int qt) { return vec + 4 * (qt % C::NSLOT) * 64; };
+  auto vec_of = [&](int qt) { return vec + (qt % C::NSLOT) * C::VSZ; };
   auto issue = [&](int qt) { issue_to(qt, q_tile(qt), vec_of(qt)); };
 
-  // S = Q K^T and dP = dO V^T of a tile, one key per lane: register 8t + j of half
-  // h holds query 16t + 8h + j of the tile.
-  auto sdp = [&](int qt, f32x16 &s, f32x16 &dp) {
-    const uint16_t *Qt = q_tile(qt), *Gt = Qt + C::TSZ;
-    bf16x8 qa[C::KST], ga[C::KST];
+  // lse and delta enter S and dP through one extra MFMA each.  MFMA row m of a tile
+  // is query swap23(m); lane m of half 0 reads that query's lse, lane m of half 1
+  // its delta, and splits -lse / scale (half 0) or -delta (half 1) into three bf16
+  // terms (hi + mid + lo = the fp32 value to ~2^-24) in K slots 0..2 of its A
+  // operand.  With B = ones in K slots 0..2 (for S) or 8..10 (for dP), the product
+  // adds -lse / scale to every element of the query's S row, and -delta to its dP
+  // row: S' = S - lse / scale gives P = exp2(c S') with c = scale log2(e), and dP'
+  // = dP - delta gives dS = P dP'.
+  const int vrow = 64 * h + swap23(ln);
+  const float xmul = h ? -1.f : -1.f / scale;
+  bf16x8 bsel_s, bsel_d;
 #pragma unroll
-    for (int st = 0; st < C::KST; ++st) {
-      qa[st] = lds_read_b128(Qt + dt_off<C::BQ>(ln, 2 * st + h));
-      ga[st] = lds_read_b128(Gt + dt_off<C::BQ>(ln, 2 * st + h));
-    }
-#pragma unroll
-    for (int st = 0; st < C::KST; ++st) {
-      s = mfma32(qa[st], kr[st], st ? s : f32x16{});
-      dp = mfma32(ga[st], vr[st], st ? dp : f32x16{});
-    }
+  for (int j = 0; j < 8; ++j) {
+    bsel_s[j] = (__bf16)((h == 0 && j < 3) ? 1.f : 0.f);
+    bsel_d[j] = (__bf16)((h == 1 && j < 3) ? 1.f : 0.f);
+  }
+  auto bcast_op = [&](float xv) {
+    const float x = xv * xmul;
+    const __bf16 hi = (__bf16)x;
+    const float r1 = x - (float)hi;
+    const __bf16 mid = (__bf16)r1;
+    const __bf16 lo = (__bf16)(r1 - (float)mid);
+    bf16x8 a = {};
+    a[0] = hi;
+    a[1] = mid;
+    a[2] = lo;
+    return a;
   };
 
-  // Transposed operands of dV^T += dO^T P and dK^T += Q^T dS for a tile, by the
-  // asm block that waits only for its own LDS reads (copies stay in flight).
-  using TOps = bf16x8[2][C::NDB];
-  auto tr_reads = [&](const uint16_t *Qt, TOps &gt, TOps &qtr) {
-    const uint16_t *Gt = Qt + C::TSZ;
+  // S' and dP' of a tile, one key per lane: register 8t + j of half h holds query
+  // 16t + 8h + j of the tile.
+  auto sdp_from = [&](const bf16x8 (&qa)[C::KST], const bf16x8 (&ga)[C::KST], float xv,
+                      f32x16 &s, f32x16 &dp) {
+    const bf16x8 av = bcast_op(xv);
+    s = mfma32(av, bsel_s, f32x16{});
+    dp = mfma32(av, bsel_d, f32x16{});
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int d = 0; d < C::NDB; ++d) {
-        gt[t][d] = dt_read_tr_perm<C::BQ>(Gt, 16 * t, d, lane);
-        qtr[t][d] = dt_read_tr_perm<C::BQ>(Qt, 16 * t, d, lane);
-      }
+    for (int st = 0; st < C::KST; ++st) {
+      s = mfma32(qa[st], kr[st], s);
+      dp = mfma32(ga[st], vr[st], dp);
+    }
+  };
+  // Operand reads of a tile for S' / dP' (b128 rows) and the lane's lse / delta.
+  auto read_q = [&](const uint16_t *__restrict__ tile, int st) {
+    return lds_read_b128(tile + dt_off<C::BQ>(ln, 2 * st + h));
+  };
+  // Transposed operand k (k < NDB: dO^T block k, else Q^T block k - NDB) of rows
+  // 16 t .. 16 t + 15 of a tile.
+  auto tr_op = [&](const uint16_t *__restrict__ tile, int t, int kk) {
+    return dt_read_tr_perm<C::BQ>(kk < C::NDB ? tile + C::TSZ : tile, 16 * t, kk % C::NDB,
+                                  lane);
   };
 
-  // P = exp(S - LSE) and dS = P (dP - delta) for elements [e0, e0 + n) of a tile.
-  auto grad_elems = [&](auto mask_tag, f32x16 &s, f32x16 &dp, const f32x4 (&L)[4],
-                        const f32x4 (&Dl)[4], int rel0, int e0, int n) {
+  // P = exp2(c S') and dS = P dP' for elements [e0, e0 + n) of a tile.
+  auto grad_elems = [&](auto mask_tag, f32x16 &s, f32x16 &dp, int rel0, int e0, int n) {
     constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
     for (int i = e0; i < e0 + n; ++i) {
       const int t = i >> 3, j = i & 7;
-      const float lj = L[2 * t + (j >> 2)][j & 3] * kLog2e;
-      const float dj = Dl[2 * t + (j >> 2)][j & 3];
-      float p = fast_exp2(fmaf(s[i], c, -lj));
+      float p = fast_exp2(s[i] * c);
       if (MASK) p = (unsigned)(rel0 + 16 * t + j) <= wm1 ? p : 0.f;
       s[i] = p;
-      dp[i] = p * (dp[i] - dj);
+      dp[i] = p * dp[i];
     }
   };
   // P enters dV as bf16 hi + lo (P = hi + lo to ~16 bits): a single bf16 P leaves
   // |dV| >= 4 outside 2e-2 of the exact gradient.
-  auto pack = [&](const f32x16 &s, const f32x16 &dp, int t, bf16x8 &ph, bf16x8 &pl,
-                  bf16x8 &ds) {
+  auto pack_p = [&](const f32x16 &s, int t, bf16x8 &ph, bf16x8 &pl) {
     ph = to_bf16x8(s, 8 * t);
 #pragma unroll
     for (int j = 0; j < 8; ++j) pl[j] = (__bf16)(s[8 * t + j] - (float)ph[j]);
-    ds = to_bf16x8(dp, 8 * t);
   };
-  auto grads = [&](const TOps &gt, const TOps &qtr, int t, const bf16x8 &ph, const bf16x8 &pl,
+  auto grads = [&](const bf16x8 (&ops)[2 * C::NDB], int d, const bf16x8 &ph, const bf16x8 &pl,
                    const bf16x8 &ds) {
-#pragma unroll
-    for (int d = 0; d < C::NDB; ++d) {
-      dva[d] = mfma32(gt[t][d], ph, dva[d]);
-      dva[d] = mfma32(gt[t][d], pl, dva[d]);
-      dka[d] = mfma32(qtr[t][d], ds, dka[d]);
-    }
-  };
-  auto read_vecs = [&](const float *vl, f32x4 (&L)[4], f32x4 (&Dl)[4]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        L[2 * t + u] = *reinterpret_cast<const f32x4 *>(vl + 16 * t + 8 * h + 4 * u);
-        Dl[2 * t + u] = *reinterpret_cast<const f32x4 *>(vl + 64 + 16 * t + 8 * h + 4 * u);
-      }
+    dva[d] = mfma32(ops[d], ph, dva[d]);
+    dva[d] = mfma32(ops[d], pl, dva[d]);
+    dka[d] = mfma32(ops[C::NDB + d], ds, dka[d]);
   };
 
   auto pin = [](float x) {
@@ -221,79 +227,133 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // One pipeline step for tile qt (S, dP in sc, dpc).  The copies of tile
-  // qt + AHEAD start first; the operands of tile qt + 1's S / dP MFMAs and tile qt's
-  // lse / delta are read; the S / dP MFMAs of tile qt + 1 (when NEXT) are issued
-  // one pair at a time between the slices of the gradient-side ALU work of tile qt;
-  // then tile qt's transposed operands are read and its dV / dK MFMAs close the
-  // step.  The tiles come in as distinct restrict pointers: with that, the compiler
-  // knows the reads do not touch the tiles being copied and does not make them wait
-  // for the copies in flight (the copies a step reads were awaited at the barrier
-  // before it).
-  auto step_body = [&](auto mask_tag, auto next_tag, int qt, f32x16 &sc, f32x16 &dpc,
-                       f32x16 &sn, f32x16 &dpn, const uint16_t *__restrict__ cur,
-                       const uint16_t *__restrict__ nxt, const float *__restrict__ vcur,
-                       uint16_t *__restrict__ dma, float *__restrict__ vdma) {
+  // One pipeline step for tile qt: S', dP' of tile qt in (sc, dpc); the S'/dP'
+  // operands (qa, ga, xv) of tile qt + 1 in registers.  LDS reads are spread over
+  // the MFMA phases so that every wave keeps its MFMAs busy while the LDS serves
+  // the reads of all four:
+  //   phase 1: S', dP' of tile qt + 1 (when NEXT) into (sn, dpn), one MFMA pair per
+  //            slice, with a transposed operand read of tile qt rows 0..15 and the
+  //            P / dS work of two (D = 128) elements per slice;
+  //   phase 2a: dV^T, dK^T of rows 0..15, one 32-column block per slice, with the
+  //            transposed operand reads of rows 16..31;
+  //   phase 2b: dV^T, dK^T of rows 16..31, with the S'/dP' operand reads of tile
+  //            qt + 2 (when LOAD) for the next step.
+  // The tiles come in as distinct restrict pointers: the compiler then knows the
+  // reads do not touch the tile being copied and does not make them wait for the
+  // copies in flight (the tiles a step reads were awaited at an earlier barrier).
+  auto step_body = [&](auto mask_tag, auto next_tag, auto load_tag, int qt, f32x16 &sc,
+                       f32x16 &dpc, f32x16 &sn, f32x16 &dpn, bf16x8 (&qa)[C::KST],
+                       bf16x8 (&ga)[C::KST], float &xv, const uint16_t *__restrict__ cur,
+                       const uint16_t *__restrict__ nn, const float *__restrict__ vnn,
+                       uint16_t *__restrict__ dma, float *__restrict__ vdma)
+                       __attribute__((always_inline)) {
     constexpr bool NEXT = decltype(next_tag)::value;
+    constexpr bool LOAD = decltype(load_tag)::value;
     if (qt + C::AHEAD <= qt1) issue_to(qt + C::AHEAD, dma, vdma);
     const int rel0 = qt * C::BQ + 8 * h - my_k;
-    bf16x8 qa[C::KST], ga[C::KST];
+    bf16x8 op0[2 * C::NDB], op1[2 * C::NDB];
     if constexpr (NEXT) {
-      const uint16_t *Gn = nxt + C::TSZ;
+      const bf16x8 av = bcast_op(xv);
+      sn = mfma32(av, bsel_s, f32x16{});
+      dpn = mfma32(av, bsel_d, f32x16{});
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int EPS = 16 / C::KST;  // elements per slice
+#pragma unroll
+    for (int st = 0; st < C::KST; ++st) {
+      op0[st] = tr_op(cur, 0, st);
+      if constexpr (NEXT) {
+        sn = mfma32(qa[st], kr[st], sn);
+        dpn = mfma32(ga[st], vr[st], dpn);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      grad_elems(mask_tag, sc, dpc, rel0, EPS * st, EPS);
+      pin(dpc[EPS * st + EPS - 1]);
+    }
+    bf16x8 ph0, pl0, ph1, pl1;
+    pack_p(sc, 0, ph0, pl0);
+    const bf16x8 ds0 = to_bf16x8(dpc, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 ds1;
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d) {
+      op1[d] = tr_op(cur, 1, d);
+      op1[C::NDB + d] = tr_op(cur, 1, C::NDB + d);
+      grads(op0, d, ph0, pl0, ds0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (d == 0) pack_p(sc, 1, ph1, pl1);
+      if (d == C::NDB - 1) ds1 = to_bf16x8(dpc, 8);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d) {
+      if constexpr (LOAD) {
+#pragma unroll
+        for (int u = 0; u < C::KST / C::NDB; ++u) {
+          const int st = (C::KST / C::NDB) * d + u;
+          qa[st] = read_q(nn, st);
+          ga[st] = read_q(nn + C::TSZ, st);
+        }
+        if (d == 0) xv = vnn[vrow];
+      }
+      grads(op1, d, ph1, pl1, ds1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto step = [&](auto mask_tag, auto next_tag, auto load_tag, int qt, f32x16 &sc, f32x16 &dpc,
+                  f32x16 &sn, f32x16 &dpn, bf16x8 (&qa)[C::KST], bf16x8 (&ga)[C::KST],
+                  float &xv) __attribute__((always_inline)) {
+    step_body(mask_tag, next_tag, load_tag, qt, sc, dpc, sn, dpn, qa, ga, xv, q_tile(qt),
+              q_tile(qt + 2), vec_of(qt + 2), q_tile(qt + C::AHEAD), vec_of(qt + C::AHEAD));
+  };
+  // S', dP' of the wave's first tile t and the S'/dP' operands of tile t + 1.
+  auto pre_body = [&](int t, f32x16 &sc, f32x16 &dpc, bf16x8 (&qa)[C::KST],
+                      bf16x8 (&ga)[C::KST], float &xv, const uint16_t *__restrict__ t0p,
+                      const float *__restrict__ v0p, const uint16_t *__restrict__ t1p,
+                      const float *__restrict__ v1p) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < C::KST; ++st) {
+      qa[st] = read_q(t0p, st);
+      ga[st] = read_q(t0p + C::TSZ, st);
+    }
+    xv = v0p[vrow];
+    sdp_from(qa, ga, xv, sc, dpc);
+    if (t + 1 <= wqt1) {
 #pragma unroll
       for (int st = 0; st < C::KST; ++st) {
-        qa[st] = lds_read_b128(nxt + dt_off<C::BQ>(ln, 2 * st + h));
-        ga[st] = lds_read_b128(Gn + dt_off<C::BQ>(ln, 2 * st + h));
+        qa[st] = read_q(t1p, st);
+        ga[st] = read_q(t1p + C::TSZ, st);
       }
+      xv = v1p[vrow];
     }
-    f32x4 L[4], Dl[4];
-    read_vecs(vcur, L, Dl);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NEXT) {
-      constexpr int EPS = 16 / C::KST;  // elements per slice
-#pragma unroll
-      for (int st = 0; st < C::KST; ++st) {
-        sn = mfma32(qa[st], kr[st], st ? sn : f32x16{});
-        dpn = mfma32(ga[st], vr[st], st ? dpn : f32x16{});
-        __builtin_amdgcn_sched_barrier(0);
-        grad_elems(mask_tag, sc, dpc, L, Dl, rel0, EPS * st, EPS);
-        pin(dpc[EPS * st + EPS - 1]);
-      }
-    } else {
-      grad_elems(mask_tag, sc, dpc, L, Dl, rel0, 0, 16);
-    }
-    TOps gt, qtr;
-    tr_reads(cur, gt, qtr);
-    bf16x8 ph0, pl0, ds0, ph1, pl1, ds1;
-    pack(sc, dpc, 0, ph0, pl0, ds0);
-    __builtin_amdgcn_sched_barrier(0);
-    grads(gt, qtr, 0, ph0, pl0, ds0);
-    pack(sc, dpc, 1, ph1, pl1, ds1);
-    grads(gt, qtr, 1, ph1, pl1, ds1);
   };
-  auto step = [&](auto mask_tag, auto next_tag, int qt, f32x16 &sc, f32x16 &dpc, f32x16 &sn,
-                  f32x16 &dpn) {
-    step_body(mask_tag, next_tag, qt, sc, dpc, sn, dpn, q_tile(qt), q_tile(qt + 1), vec_of(qt),
-              q_tile(qt + C::AHEAD), vec_of(qt + C::AHEAD));
-  };
-  // End of step qt: the tile needed next (copied a step earlier) must have landed;
-  // the copies this step issued (tile qt + AHEAD) may stay in flight.
+  // End of step qt: tile qt + 3 (copied a step earlier) must have landed; the copies
+  // this step issued (tile qt + AHEAD) may stay in flight.  Before every step qt,
+  // tiles up to qt + 2 have landed and are visible to all waves.
   auto sync = [&](int qt) {
     if (qt + C::AHEAD <= qt1) __builtin_amdgcn_s_waitcnt(kWaitVm<C::NCOPY>);
     else __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
     lds_barrier();
   };
 
-  // prologue: tiles qt0 .. qt0 + AHEAD - 1; all but the last must have landed
+  // prologue: tiles qt0 .. qt0 + AHEAD - 1 in flight; those up to qt0 + 2 must land
   for (int t = qt0; t < qt0 + C::AHEAD && t <= qt1; ++t) issue(t);
-  sync(qt0 - 1);
-  f32x16 sc, dpc, sn, dpn;
-  if (wqt0 == qt0) sdp(qt0, sc, dpc);
+  if (qt0 + C::AHEAD - 1 <= qt1) __builtin_amdgcn_s_waitcnt(kWaitVm<C::NCOPY>);
+  else __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+  lds_barrier();
 
-  // Phases of the wave: idle tiles, S / dP of its first tile, the diagonal tile
-  // (masked), unmasked tiles, tiles crossing the window's far edge (masked), the
-  // last tile (no S / dP ahead), idle tiles.  One barrier per tile of the
-  // workgroup in every phase.
+  f32x16 sa, dpa, sb, dpb;
+  bf16x8 qa[C::KST], ga[C::KST];
+  float xv = 0.f;
+  if (wqt0 == qt0)
+    pre_body(qt0, sa, dpa, qa, ga, xv, q_tile(qt0), vec_of(qt0), q_tile(qt0 + 1),
+             vec_of(qt0 + 1));
+
+  // Phases of the wave: idle tiles, the step before its first tile (S', dP' of that
+  // tile), its tiles (the first one and those from mlo on masked), idle tiles.  One
+  // barrier per tile of the workgroup in every phase.
+  using F = std::false_type;
+  using Tr = std::true_type;
   int qt = qt0;
   for (; qt < min(wqt0 - 1, qt1 + 1); ++qt) {
     if (qt + C::AHEAD <= qt1) issue(qt + C::AHEAD);
@@ -301,32 +361,62 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   }
   if (wqt0 > qt0 && qt == wqt0 - 1) {
     if (qt + C::AHEAD <= qt1) issue(qt + C::AHEAD);
-    sdp(qt + 1, sc, dpc);
+    pre_body(qt + 1, sa, dpa, qa, ga, xv, q_tile(qt + 1), vec_of(qt + 1), q_tile(qt + 2),
+             vec_of(qt + 2));
     sync(qt);
     ++qt;
   }
-  auto advance = [&] {
-    sc = sn;
-    dpc = dpn;
+  // The wave's tiles wqt0 .. wqt1; S' / dP' of tile qt in (sa, dpa) between steps.
+  // Step qt computes S' / dP' of tile qt + 1 when qt < wqt1 (NEXT) and reads the
+  // operands of tile qt + 2 when qt + 2 <= wqt1 (LOAD); tile wqt0 and tiles from mlo
+  // on are masked.
+  auto next = [&] {
+    sa = sb;
+    dpa = dpb;
   };
-  if (qt == wqt0 && qt < wqt1) {  // diagonal tile
-    step(std::true_type{}, std::true_type{}, qt, sc, dpc, sn, dpn);
-    advance();
+  if (qt == wqt0 && qt <= wqt1) {  // diagonal tile
+    if (qt + 2 <= wqt1) {
+      step(Tr{}, Tr{}, Tr{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
+      next();
+    } else if (qt + 1 <= wqt1) {
+      step(Tr{}, Tr{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
+      next();
+    } else {
+      step(Tr{}, F{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
+    }
     sync(qt);
     ++qt;
   }
-  for (; qt < min(wqt1, mlo); ++qt) {
-    step(std::false_type{}, std::true_type{}, qt, sc, dpc, sn, dpn);
-    advance();
+  // unmasked steps with NEXT and LOAD, two per iteration (no register copies)
+  const int ulim = min(wqt1 - 1, mlo);
+  for (; qt + 1 < ulim; qt += 2) {
+    step(F{}, Tr{}, Tr{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
+    sync(qt);
+    step(F{}, Tr{}, Tr{}, qt + 1, sb, dpb, sa, dpa, qa, ga, xv);
+    sync(qt + 1);
+  }
+  if (qt < ulim) {
+    step(F{}, Tr{}, Tr{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
+    next();
+    sync(qt);
+    ++qt;
+  }
+  // masked steps with NEXT and LOAD
+  for (; qt < wqt1 - 1; ++qt) {
+    step(Tr{}, Tr{}, Tr{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
+    next();
     sync(qt);
   }
-  for (; qt < wqt1; ++qt) {
-    step(std::true_type{}, std::true_type{}, qt, sc, dpc, sn, dpn);
-    advance();
+  if (qt == wqt1 - 1) {
+    if (qt >= mlo) step(Tr{}, Tr{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
+    else step(F{}, Tr{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
+    next();
     sync(qt);
+    ++qt;
   }
   if (qt == wqt1) {
-    step(std::true_type{}, std::false_type{}, qt, sc, dpc, sn, dpn);
+    if (qt >= mlo) step(Tr{}, F{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
+    else step(F{}, F{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
     sync(qt);
     ++qt;
   }
