@@ -270,11 +270,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     dpc = dpn;
     sync();
   }
-  for (; kt < wkt1; ++kt) {
+  // unmasked tiles, two per iteration: S / dP of the next tile alternate between the
+  // two register sets, so nothing is copied
+  for (; kt + 1 < wkt1; kt += 2) {
+    step(std::false_type{}, kt, sc, dpc, sn, dpn);
+    sync();
+    step(std::false_type{}, kt + 1, sn, dpn, sc, dpc);
+    sync();
+  }
+  if (kt < wkt1) {
     step(std::false_type{}, kt, sc, dpc, sn, dpn);
     sc = sn;
     dpc = dpn;
     sync();
+    ++kt;
   }
   if (kt == wkt1) {
     last_step(kt, sc, dpc);

@@ -27,8 +27,8 @@ template <int D>
 struct DkdvCfg {
   static constexpr int BK = 128;          // keys per workgroup (4 waves x 32)
   static constexpr int BQ = 32;           // queries per tile
-  static constexpr int NSLOT = 5;         // LDS tile slots (tile t in slot t % 5)
-  static constexpr int AHEAD = NSLOT - 1; // tiles are copied this many steps ahead
+  static constexpr int NSLOT = 8;         // LDS tile slots (tile t in slot t % 8)
+  static constexpr int AHEAD = 4;         // tiles are copied this many steps ahead
   static constexpr int TSZ = BQ * D;      // elements of one Q (or dO) tile
   static constexpr int NDB = D / 32;
   static constexpr int KST = D / 16;      // = 2 * NDB
@@ -41,6 +41,9 @@ struct DkdvCfg {
 
 // s_waitcnt immediate: at most N vector-memory operations of the wave in flight;
 // LDS operations and exports not waited for.
+// Largest P of a tile (any lane) from which P enters dV as bf16 hi + lo.
+constexpr float kLoP = 0.0625f;
+
 template <int N>
 constexpr int kWaitVm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
 
@@ -139,8 +142,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void *)(vdst + w * 64), 4, lane * 4, 0, 0, 0);
   };
-  auto q_tile = [&](int qt) { return smem + 2 * (qt % C::NSLOT) * C::TSZ; };
-  auto vec_of = [&](int qt) { return vec + (qt % C::NSLOT) * C::VSZ; };
+  auto q_tile = [&](int qt) { return smem + 2 * (qt & (C::NSLOT - 1)) * C::TSZ; };
+  auto vec_of = [&](int qt) { return vec + (qt & (C::NSLOT - 1)) * C::VSZ; };
   auto issue = [&](int qt) { issue_to(qt, q_tile(qt), vec_of(qt)); };
 
   // lse and delta enter S and dP through one extra MFMA each.  MFMA row m of a tile
@@ -196,8 +199,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
                                   lane);
   };
 
-  // P = exp2(c S') and dS = P dP' for elements [e0, e0 + n) of a tile.
-  auto grad_elems = [&](auto mask_tag, f32x16 &s, f32x16 &dp, int rel0, int e0, int n) {
+  // P = exp2(c S') and dS = P dP' for elements [e0, e0 + n) of a tile; pm keeps the
+  // largest P of the lane.
+  auto grad_elems = [&](auto mask_tag, f32x16 &s, f32x16 &dp, float &pm, int rel0, int e0,
+                        int n) {
     constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
     for (int i = e0; i < e0 + n; ++i) {
@@ -207,18 +212,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       s[i] = p;
       dp[i] = p * dp[i];
     }
-  };
-  // P enters dV as bf16 hi + lo (P = hi + lo to ~16 bits): a single bf16 P leaves
-  // |dV| >= 4 outside 2e-2 of the exact gradient.
-  auto pack_p = [&](const f32x16 &s, int t, bf16x8 &ph, bf16x8 &pl) {
-    ph = to_bf16x8(s, 8 * t);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pl[j] = (__bf16)(s[8 * t + j] - (float)ph[j]);
+    for (int i = e0; i < e0 + n; i += 2) pm = fmaxf(pm, fmaxf(s[i], s[i + 1]));
   };
-  auto grads = [&](const bf16x8 (&ops)[2 * C::NDB], int d, const bf16x8 &ph, const bf16x8 &pl,
-                   const bf16x8 &ds) {
+  // P enters dV as bf16.  Where some P of the wave's tile reaches kLoP, it enters as
+  // hi + lo instead: hi = P truncated to bf16, lo = the exact remainder rounded to
+  // bf16 (P = hi + lo to ~2^-16 relative).  A single bf16 P on those large values
+  // leaves |dV| >= 4 outside 2e-2 of the exact gradient; below kLoP the rounding of
+  // P (<= 2^-13 absolute) is far inside it.
+  auto pack_rne = [&](const f32x16 &s, int t) { return to_bf16x8(s, 8 * t); };
+  auto pack_hilo = [&](const f32x16 &s, int t, bf16x8 &ph, bf16x8 &pl) {
+    u32x4 hp, lp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = s[8 * t + 2 * j], b = s[8 * t + 2 * j + 1];
+      const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+      hp[j] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+      const bf16x2 r = {(__bf16)(a - __uint_as_float(ua & 0xffff0000u)),
+                        (__bf16)(b - __uint_as_float(ub & 0xffff0000u))};
+      lp[j] = __builtin_bit_cast(uint32_t, r);
+    }
+    ph = __builtin_bit_cast(bf16x8, hp);
+    pl = __builtin_bit_cast(bf16x8, lp);
+  };
+  auto grads = [&](bool lo, const bf16x8 (&ops)[2 * C::NDB], int d, const bf16x8 &ph,
+                   const bf16x8 &pl, const bf16x8 &ds) {
     dva[d] = mfma32(ops[d], ph, dva[d]);
-    dva[d] = mfma32(ops[d], pl, dva[d]);
+    if (lo) dva[d] = mfma32(ops[d], pl, dva[d]);
     dka[d] = mfma32(ops[C::NDB + d], ds, dka[d]);
   };
 
@@ -252,6 +272,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     if (qt + C::AHEAD <= qt1) issue_to(qt + C::AHEAD, dma, vdma);
     const int rel0 = qt * C::BQ + 8 * h - my_k;
     bf16x8 op0[2 * C::NDB], op1[2 * C::NDB];
+    float pm = 0.f;
     if constexpr (NEXT) {
       const bf16x8 av = bcast_op(xv);
       sn = mfma32(av, bsel_s, f32x16{});
@@ -267,11 +288,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
         dpn = mfma32(ga[st], vr[st], dpn);
       }
       __builtin_amdgcn_sched_barrier(0);
-      grad_elems(mask_tag, sc, dpc, rel0, EPS * st, EPS);
+      grad_elems(mask_tag, sc, dpc, pm, rel0, EPS * st, EPS);
       pin(dpc[EPS * st + EPS - 1]);
     }
+    // phases 2a and 2b; the lo part of P only where the tile holds a large P
+    const bool lo = __builtin_amdgcn_ballot_w64(pm >= kLoP) != 0;
     bf16x8 ph0, pl0, ph1, pl1;
-    pack_p(sc, 0, ph0, pl0);
+    if (lo) pack_hilo(sc, 0, ph0, pl0);
+    else ph0 = pack_rne(sc, 0);
     const bf16x8 ds0 = to_bf16x8(dpc, 0);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 ds1;
@@ -279,9 +303,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     for (int d = 0; d < C::NDB; ++d) {
       op1[d] = tr_op(cur, 1, d);
       op1[C::NDB + d] = tr_op(cur, 1, C::NDB + d);
-      grads(op0, d, ph0, pl0, ds0);
+      grads(lo, op0, d, ph0, pl0, ds0);
       __builtin_amdgcn_sched_barrier(0);
-      if (d == 0) pack_p(sc, 1, ph1, pl1);
+      if (d == 0) {
+        if (lo) pack_hilo(sc, 1, ph1, pl1);
+        else ph1 = pack_rne(sc, 1);
+      }
       if (d == C::NDB - 1) ds1 = to_bf16x8(dpc, 8);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -296,7 +323,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
         }
         if (d == 0) xv = vnn[vrow];
       }
-      grads(op1, d, ph1, pl1, ds1);
+      grads(lo, op1, d, ph1, pl1, ds1);
       __builtin_amdgcn_sched_barrier(0);
     }
   };

@@ -166,16 +166,21 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 #pragma unroll
       for (int d = 0; d < C::NDB; ++d) va[t][d] = dt_read_tr<C::BN>(Vt, 16 * t, d, lane);
   };
-  // O rescale (when some row max moved) and O += P V of a tile.
+  // O rescale (when some row max moved) and O += P V of a tile.  The PV MFMAs are
+  // issued at raised wave priority: with two waves per SIMD, the one holding a
+  // run of MFMAs then keeps the matrix unit busy while the other issues vector
+  // work in between.
   auto finish = [&](bool need, float alpha, const VOps &va, const bf16x8 (&p)[2]) {
     if (need) {
 #pragma unroll
       for (int d = 0; d < C::NDB; ++d) acc[d] *= alpha;
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int d = 0; d < C::NDB; ++d) acc[d] = mfma32(va[t][d], p[t], acc[d]);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Softmax of tile kt (S in sc) with the S MFMAs of tile kt + 1 (into sn) issued
@@ -296,10 +301,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     sc = sn;
     sync();
   }
-  for (; kt < wkt1; ++kt) {
+  // unmasked tiles, two per iteration: S of the next tile alternates between sc and
+  // sn, so no registers are copied
+  for (; kt + 1 < wkt1; kt += 2) {
+    step(std::false_type{}, [&] { loads(kt); }, k_next(kt), v_cur(kt), kt * C::BN, sc, sn);
+    sync();
+    step(std::false_type{}, [&] { loads(kt + 1); }, k_next(kt + 1), v_cur(kt + 1),
+         (kt + 1) * C::BN, sn, sc);
+    sync();
+  }
+  if (kt < wkt1) {
     step(std::false_type{}, [&] { loads(kt); }, k_next(kt), v_cur(kt), kt * C::BN, sc, sn);
     sc = sn;
     sync();
+    ++kt;
   }
   if (kt == wkt1) {  // the diagonal tile: no S to compute ahead
     VOps va;
