@@ -7,6 +7,7 @@ Every call recompiles; the result is ``causal_sliding_window_amd/libswattn.so``.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -27,6 +28,8 @@ HIPCC_FLAGS = [
     # no packed-fp32 instructions anywhere (they are avoided on this hardware)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # per-kernel register / scratch report, checked below
+    "-Rpass-analysis=kernel-resource-usage",
 ]
 # Per-source extra flags.  Most kernels keep MFMA results in arch VGPRs, where
 # they feed ALU work (avoids accumulator <-> VGPR copies); the dK/dV kernel keeps
@@ -42,8 +45,37 @@ def hipcc() -> str:
     return exe
 
 
+def resource_report(remarks: str) -> dict:
+    """Per-kernel resource figures from the compiler's kernel-resource-usage remarks."""
+    kernels, cur = {}, None
+    for line in remarks.splitlines():
+        if "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].split("[-Rpass", 1)[0].strip()
+        if body.startswith("Function Name:"):
+            cur = kernels.setdefault(body.split(":", 1)[1].strip(), {})
+        elif cur is not None and ":" in body:
+            key, val = body.rsplit(":", 1)
+            cur[key.strip()] = val.strip()
+    return kernels
+
+
+def check_resources(source: str, kernels: dict) -> list:
+    """Kernels that spill vector registers or use per-lane scratch memory: every kernel
+    must run without either (that traffic goes to HBM on every launch).  Scalar
+    spills into vector-register lanes (scratch 0) stay on chip and are allowed."""
+    bad = []
+    for name, r in kernels.items():
+        scratch = int(r.get("ScratchSize [bytes/lane]", "0") or 0)
+        spills = int(r.get("VGPRs Spill", "0") or 0)
+        if scratch or spills:
+            bad.append(f"{source}: {name}: scratch {scratch} B/lane, {spills} spilled VGPRs")
+    return bad
+
+
 def build(verbose: bool = False, csrc: str = CSRC, out: str = LIB) -> str:
-    """Compile every source to an object (in parallel), then link the library."""
+    """Compile every source to an object (in parallel), then link the library.  Fails
+    when a kernel spills registers or uses scratch memory."""
     noise = "not a recognized feature for this target"
     with tempfile.TemporaryDirectory(prefix="swattn_build_") as tmpdir:
         procs, objs = [], []
@@ -62,8 +94,18 @@ def build(verbose: bool = False, csrc: str = CSRC, out: str = LIB) -> str:
             err = "\n".join(l for l in err.splitlines() if noise not in l)
             if p.returncode != 0:
                 errors.append(f"{s}: hipcc failed ({p.returncode}):\n{err}")
-            elif verbose and err.strip():
-                print(err, file=sys.stderr)
+                continue
+            kernels = resource_report(err)
+            errors.extend(check_resources(s, kernels))
+            if verbose:
+                for name, r in kernels.items():
+                    print(f"{s}: {name[:60]}: VGPRs {r.get('VGPRs')} AGPRs {r.get('AGPRs')} "
+                          f"LDS {r.get('LDS Size [bytes/block]')} occupancy "
+                          f"{r.get('Occupancy [waves/SIMD]')}", file=sys.stderr)
+                rest = "\n".join(l for l in err.splitlines()
+                                 if "remark:" not in l and not re.match(r"\s*(\d+ )?\|", l))
+                if rest.strip():
+                    print(rest, file=sys.stderr)
         if errors:
             raise RuntimeError("\n".join(errors))
         tmp = out + ".tmp"

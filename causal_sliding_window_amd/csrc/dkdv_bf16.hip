@@ -395,8 +395,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   }
   // The wave's tiles wqt0 .. wqt1; S' / dP' of tile qt in (sa, dpa) between steps.
   // Step qt computes S' / dP' of tile qt + 1 when qt < wqt1 (NEXT) and reads the
-  // operands of tile qt + 2 when qt + 2 <= wqt1 (LOAD); tile wqt0 and tiles from mlo
-  // on are masked.
+  // operands of tile qt + 2 when qt + 2 <= wqt1 (LOAD); tile wqt0, tiles from mlo on
+  // and the last two tiles run the element mask.
   auto next = [&] {
     sa = sb;
     dpa = dpb;
@@ -434,16 +434,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     next();
     sync(qt);
   }
+  // the last two steps always run the element mask (it keeps every element of an
+  // unmasked tile): one code path each
   if (qt == wqt1 - 1) {
-    if (qt >= mlo) step(Tr{}, Tr{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
-    else step(F{}, Tr{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
+    step(Tr{}, Tr{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
     next();
     sync(qt);
     ++qt;
   }
   if (qt == wqt1) {
-    if (qt >= mlo) step(Tr{}, F{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
-    else step(F{}, F{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
+    step(Tr{}, F{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
     sync(qt);
     ++qt;
   }
