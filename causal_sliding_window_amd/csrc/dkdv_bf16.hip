@@ -235,11 +235,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     ph = __builtin_bit_cast(bf16x8, hp);
     pl = __builtin_bit_cast(bf16x8, lp);
   };
-  auto grads = [&](bool lo, const bf16x8 (&ops)[2 * C::NDB], int d, const bf16x8 &ph,
-                   const bf16x8 &pl, const bf16x8 &ds) {
+  auto grads = [&](const bf16x8 (&ops)[2 * C::NDB], int d, const bf16x8 &ph,
+                   const bf16x8 &ds) {
     dva[d] = mfma32(ops[d], ph, dva[d]);
-    if (lo) dva[d] = mfma32(ops[d], pl, dva[d]);
     dka[d] = mfma32(ops[C::NDB + d], ds, dka[d]);
+  };
+  auto grads_lo = [&](const bf16x8 (&ops)[2 * C::NDB], const bf16x8 &pl) {
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d) dva[d] = mfma32(ops[d], pl, dva[d]);
   };
 
   auto pin = [](float x) {
@@ -291,11 +294,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       grad_elems(mask_tag, sc, dpc, pm, rel0, EPS * st, EPS);
       pin(dpc[EPS * st + EPS - 1]);
     }
-    // phases 2a and 2b; the lo part of P only where the tile holds a large P
+    // phases 2a and 2b; the lo part of P only where the tile holds a large P, its
+    // MFMAs grouped after each phase (one branch per group)
     const bool lo = __builtin_amdgcn_ballot_w64(pm >= kLoP) != 0;
     bf16x8 ph0, pl0, ph1, pl1;
-    if (lo) pack_hilo(sc, 0, ph0, pl0);
-    else ph0 = pack_rne(sc, 0);
+    if (lo) {
+      pack_hilo(sc, 0, ph0, pl0);
+      pack_hilo(sc, 1, ph1, pl1);
+    } else {
+      ph0 = pack_rne(sc, 0);
+      ph1 = pack_rne(sc, 1);
+    }
     const bf16x8 ds0 = to_bf16x8(dpc, 0);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 ds1;
@@ -303,15 +312,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     for (int d = 0; d < C::NDB; ++d) {
       op1[d] = tr_op(cur, 1, d);
       op1[C::NDB + d] = tr_op(cur, 1, C::NDB + d);
-      grads(lo, op0, d, ph0, pl0, ds0);
+      grads(op0, d, ph0, ds0);
       __builtin_amdgcn_sched_barrier(0);
-      if (d == 0) {
-        if (lo) pack_hilo(sc, 1, ph1, pl1);
-        else ph1 = pack_rne(sc, 1);
-      }
       if (d == C::NDB - 1) ds1 = to_bf16x8(dpc, 8);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (lo) grads_lo(op0, pl0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int d = 0; d < C::NDB; ++d) {
       if constexpr (LOAD) {
@@ -323,9 +330,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
         }
         if (d == 0) xv = vnn[vrow];
       }
-      grads(lo, op1, d, ph1, pl1, ds1);
+      grads(op1, d, ph1, ds1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (lo) grads_lo(op1, pl1);
   };
   auto step = [&](auto mask_tag, auto next_tag, auto load_tag, int qt, f32x16 &sc, f32x16 &dpc,
                   f32x16 &sn, f32x16 &dpn, bf16x8 (&qa)[C::KST], bf16x8 (&ga)[C::KST],
