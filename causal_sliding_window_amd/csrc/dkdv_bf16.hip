@@ -123,24 +123,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   const int rl = lane >> 2;
   const int lc = (lane & 3) ^ ((lane >> 4) & 3);  // logical chunk stored at this position
   const uint32_t lane_off = (swap23(rl) * rs + 8 * lc) * 2;
+  // One buffer resource per tensor over all T rows of this (b, h): a tile's row
+  // offset goes into the lane offsets, and offsets from row T on read as zero.
+  const int my_tensor = (w * C::CPW) / C::HALF;  // every copy of a wave is Q (0) or dO (1)
+  const __amdgpu_buffer_rsrc_t rsrc_t = make_rsrc(my_tensor ? gb : qb, (uint32_t)T * rs * 2);
+  const __amdgpu_buffer_rsrc_t rsrc_v = make_rsrc((w & 1) ? delb : lseb, (uint32_t)T * 4);
   auto issue_to = [&](int qt, uint16_t *tile, float *vdst) {
-    const int row0 = qt * C::BQ;
-    const uint32_t nbytes = (uint32_t)(T - row0) * rs * 2;
+    const uint32_t roff = (uint32_t)(qt * C::BQ) * (uint32_t)rs * 2;
 #pragma unroll
     for (int cc = 0; cc < C::CPW; ++cc) {
-      const int j = w * C::CPW + cc;
-      const int tensor = j / C::HALF, jj = j % C::HALF;
+      const int jj = (w * C::CPW + cc) % C::HALF;
       const int db = jj / C::RG, row16 = 16 * (jj % C::RG);
-      const __amdgpu_buffer_rsrc_t r = make_rsrc((tensor ? gb : qb) + (size_t)row0 * rs, nbytes);
-      buf_copy16_to_lds(r, tile + tensor * C::TSZ + db * (C::BQ * 32) + row16 * 32,
-                        lane_off + (row16 * rs + 32 * db) * 2);
+      buf_copy16_to_lds(rsrc_t, tile + my_tensor * C::TSZ + db * (C::BQ * 32) + row16 * 32,
+                        lane_off + (uint32_t)(row16 * rs + 32 * db) * 2 + roff);
     }
     // every wave issues exactly NCOPY copies per tile (waves 2 and 3 fill spare
     // rows), so the end-of-step wait can count them
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(((w & 1) ? delb : lseb) + row0, (uint32_t)(T - row0) * 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void *)(vdst + w * 64), 4, lane * 4, 0, 0, 0);
+        rsrc_v, (__attribute__((address_space(3))) void *)(vdst + w * 64), 4,
+        (uint32_t)(lane + qt * C::BQ) * 4, 0, 0, 0);
   };
   auto q_tile = [&](int qt) { return smem + 2 * (qt & (C::NSLOT - 1)) * C::TSZ; };
   auto vec_of = [&](int qt) { return vec + (qt & (C::NSLOT - 1)) * C::VSZ; };
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
                        __attribute__((always_inline)) {
     constexpr bool NEXT = decltype(next_tag)::value;
     constexpr bool LOAD = decltype(load_tag)::value;
-    if (qt + C::AHEAD <= qt1) issue_to(qt + C::AHEAD, dma, vdma);
+    issue_to(qt + C::AHEAD, dma, vdma);
     const int rel0 = qt * C::BQ + 8 * h - my_k;
     bf16x8 op0[2 * C::NDB], op1[2 * C::NDB];
     float pm = 0.f;
@@ -364,17 +365,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   };
   // End of step qt: tile qt + 3 (copied a step earlier) must have landed; the copies
   // this step issued (tile qt + AHEAD) may stay in flight.  Before every step qt,
-  // tiles up to qt + 2 have landed and are visible to all waves.
-  auto sync = [&](int qt) {
-    if (qt + C::AHEAD <= qt1) __builtin_amdgcn_s_waitcnt(kWaitVm<C::NCOPY>);
-    else __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+  // tiles up to qt + 2 have landed and are visible to all waves.  Every step issues
+  // its copies, also past the workgroup's last tile (rows from T on read as zero
+  // and land in slots no step reads), so the wait count is always the same.
+  auto sync = [&](int) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm<C::NCOPY>);
     lds_barrier();
   };
 
   // prologue: tiles qt0 .. qt0 + AHEAD - 1 in flight; those up to qt0 + 2 must land
-  for (int t = qt0; t < qt0 + C::AHEAD && t <= qt1; ++t) issue(t);
-  if (qt0 + C::AHEAD - 1 <= qt1) __builtin_amdgcn_s_waitcnt(kWaitVm<C::NCOPY>);
-  else __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
+  for (int t = qt0; t < qt0 + C::AHEAD; ++t) issue(t);
+  __builtin_amdgcn_s_waitcnt(kWaitVm<C::NCOPY>);
   lds_barrier();
 
   f32x16 sa, dpa, sb, dpb;
@@ -391,11 +392,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   using Tr = std::true_type;
   int qt = qt0;
   for (; qt < min(wqt0 - 1, qt1 + 1); ++qt) {
-    if (qt + C::AHEAD <= qt1) issue(qt + C::AHEAD);
+    issue(qt + C::AHEAD);
     sync(qt);
   }
   if (wqt0 > qt0 && qt == wqt0 - 1) {
-    if (qt + C::AHEAD <= qt1) issue(qt + C::AHEAD);
+    issue(qt + C::AHEAD);
     pre_body(qt + 1, sa, dpa, qa, ga, xv, q_tile(qt + 1), vec_of(qt + 1), q_tile(qt + 2),
              vec_of(qt + 2));
     sync(qt);
@@ -456,9 +457,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     ++qt;
   }
   for (; qt <= qt1; ++qt) {
-    if (qt + C::AHEAD <= qt1) issue(qt + C::AHEAD);
+    issue(qt + C::AHEAD);
     sync(qt);
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm<0>);  // no copy into LDS outlives the workgroup
 
   if (my_k < T) {
     uint16_t *dkb = dk + base + (size_t)my_k * rs, *dvb = dv + base + (size_t)my_k * rs;
