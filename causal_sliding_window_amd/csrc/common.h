@@ -143,6 +143,11 @@ __device__ __forceinline__ bf16x8 dt_read_tr(const uint16_t *tile, int row0, int
              lds_read_tr(sub + r2 * 32 + 8 * (lc ^ ((r2 >> 2) & 3)) + w));
 }
 
+// s_waitcnt immediate: at most N vector-memory operations of the wave in flight;
+// LDS operations and exports not waited for.
+template <int N>
+constexpr int kWaitVm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+
 // Workgroup barrier for handing LDS tiles between waves.  The caller first waits
 // (s_waitcnt) for what must be complete: its own copies into the tiles about to be
 // read (vmcnt) and its own LDS reads of the tiles about to be overwritten

@@ -39,13 +39,8 @@ struct DkdvCfg {
   static constexpr int VSZ = 256;              // floats of lse / delta per slot
 };
 
-// s_waitcnt immediate: at most N vector-memory operations of the wave in flight;
-// LDS operations and exports not waited for.
 // Largest P of a tile (any lane) from which P enters dV as bf16 hi + lo.
 constexpr float kLoP = 0.0625f;
-
-template <int N>
-constexpr int kWaitVm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
