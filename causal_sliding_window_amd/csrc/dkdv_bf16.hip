@@ -28,7 +28,7 @@ struct DkdvCfg {
   static constexpr int BK = 128;          // keys per workgroup (4 waves x 32)
   static constexpr int BQ = 32;           // queries per tile
   static constexpr int NSLOT = 8;         // LDS tile slots (tile t in slot t % 8)
-  static constexpr int AHEAD = 4;         // tiles are copied this many steps ahead
+  static constexpr int AHEAD = 6;         // tiles are copied this many steps ahead
   static constexpr int TSZ = BQ * D;      // elements of one Q (or dO) tile
   static constexpr int NDB = D / 32;
   static constexpr int KST = D / 16;      // = 2 * NDB
@@ -358,19 +358,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       xv = v1p[vrow];
     }
   };
-  // End of step qt: tile qt + 3 (copied a step earlier) must have landed; the copies
-  // this step issued (tile qt + AHEAD) may stay in flight.  Before every step qt,
-  // tiles up to qt + 2 have landed and are visible to all waves.  Every step issues
+  // One barrier per two steps, after the steps qt with qt - qt0 odd: there, all
+  // copies but those of the last two steps (tiles qt + AHEAD - 1, qt + AHEAD) must
+  // have landed, so that the next two steps find tiles up to qt + 4 in LDS.  A step
+  // reads tiles qt .. qt + 2 and copies into the slot of tile qt - 2, both of them
+  // separated from the other uses of those slots by a barrier.  Every step issues
   // its copies, also past the workgroup's last tile (rows from T on read as zero
   // and land in slots no step reads), so the wait count is always the same.
-  auto sync = [&](int) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm<C::NCOPY>);
-    lds_barrier();
+  auto sync = [&](int qt) {
+    if ((qt - qt0) & 1) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm<2 * C::NCOPY>);
+      lds_barrier();
+    }
   };
 
-  // prologue: tiles qt0 .. qt0 + AHEAD - 1 in flight; those up to qt0 + 2 must land
+  // prologue: tiles qt0 .. qt0 + AHEAD - 1 in flight; those up to qt0 + 3 must land
   for (int t = qt0; t < qt0 + C::AHEAD; ++t) issue(t);
-  __builtin_amdgcn_s_waitcnt(kWaitVm<C::NCOPY>);
+  __builtin_amdgcn_s_waitcnt(kWaitVm<2 * C::NCOPY>);
   lds_barrier();
 
   f32x16 sa, dpa, sb, dpb;
