@@ -55,7 +55,8 @@ template <int D>
 struct DqCfg {
   static constexpr int BM = 128;          // queries per workgroup (4 waves x 32)
   static constexpr int BN = 32;           // keys per tile
-  static constexpr int NSLOT = 3;         // LDS tile slots (tile t in slot t % 3)
+  static constexpr int NSLOT = 4;         // LDS tile slots (tile t in slot t % 4)
+  static constexpr int AHEAD = 3;         // tiles are copied this many steps ahead
   static constexpr int TSZ = BN * D;      // elements of one K (or V) tile
   static constexpr int NDB = D / 32;
   static constexpr int KST = D / 16;
@@ -143,21 +144,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const int rl = lane >> 2;
   const int lc = (lane & 3) ^ ((lane >> 4) & 3);  // logical chunk stored at this position
   const uint32_t lane_off = (swap23(rl) * rs + 8 * lc) * 2;
+  // One buffer resource per tensor over all T rows of this (b, h): a tile's row
+  // offset goes into the lane offsets, and offsets from row T on read as zero.
+  const int my_tensor = (w * C::CPW) / C::HALF;  // every copy of a wave is K (0) or V (1)
+  const __amdgpu_buffer_rsrc_t rsrc_t = make_rsrc(my_tensor ? vb : kb, (uint32_t)T * rs * 2);
   auto issue = [&](int kt) {
-    const int slot = kt % C::NSLOT;
-    const int row0 = kt * C::BN;
-    const uint32_t nbytes = (uint32_t)(T - row0) * rs * 2;
+    const int slot = kt & (C::NSLOT - 1);
+    const uint32_t roff = (uint32_t)(kt * C::BN) * (uint32_t)rs * 2;
 #pragma unroll
     for (int cc = 0; cc < C::CPW; ++cc) {
-      const int j = w * C::CPW + cc;
-      const int tensor = j / C::HALF, jj = j % C::HALF;
+      const int jj = (w * C::CPW + cc) % C::HALF;
       const int db = jj / C::RG, row16 = 16 * (jj % C::RG);
-      const __amdgpu_buffer_rsrc_t r = make_rsrc((tensor ? vb : kb) + (size_t)row0 * rs, nbytes);
-      buf_copy16_to_lds(r, smem + (2 * slot + tensor) * C::TSZ + db * (C::BN * 32) + row16 * 32,
-                        lane_off + (row16 * rs + 32 * db) * 2);
+      buf_copy16_to_lds(rsrc_t,
+                        smem + (2 * slot + my_tensor) * C::TSZ + db * (C::BN * 32) + row16 * 32,
+                        lane_off + (uint32_t)(row16 * rs + 32 * db) * 2 + roff);
     }
   };
-  auto k_tile = [&](int kt) { return smem + 2 * (kt % C::NSLOT) * C::TSZ; };
+  auto k_tile = [&](int kt) { return smem + 2 * (kt & (C::NSLOT - 1)) * C::TSZ; };
 
   // S^T = K Q^T and dP^T = V dO^T of a tile, one query per lane: register i of half
   // h holds key c_row(i, h) of the tile.
@@ -203,11 +206,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // One pipeline step for tile kt (S^T, dP^T in sc, dpc): the copies of tile kt + 2
+  // One pipeline step for tile kt (S^T, dP^T in sc, dpc): the copies of tile kt + 3
   // start first; the S / dP MFMAs of tile kt + 1 are issued one pair at a time
   // between the slices of tile kt's dS work, then dQ += dS K for tile kt.
   auto step = [&](auto mask_tag, int kt, f32x16 &sc, f32x16 &dpc, f32x16 &sn, f32x16 &dpn) {
-    if (kt + 2 <= kt1) issue(kt + 2);
+    issue(kt + C::AHEAD);
     const uint16_t *Kn = k_tile(kt + 1), *Vn = Kn + C::TSZ;
     // operands are read AHEAD slices before their MFMAs
     constexpr int AHEAD = 2;
@@ -233,18 +236,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     dq_mfma(kt, dpc);
   };
   auto last_step = [&](int kt, f32x16 &sc, f32x16 &dpc) {
-    if (kt + 2 <= kt1) issue(kt + 2);
+    issue(kt + C::AHEAD);
     ds_elems(std::true_type{}, sc, dpc, my_q - kt * C::BN - 8 * h, 0, 16);
     dq_mfma(kt, dpc);
   };
+  // End of step kt: tile kt + 2 (copied a step earlier) must have landed; the copies
+  // of this step (tile kt + AHEAD) may stay in flight.  Before every step kt, tiles
+  // up to kt + 1 have landed and are visible to all waves.  Every step issues its
+  // copies, also past the workgroup's last tile (rows from T on read as zero and
+  // land in slots no step reads), so the wait count is always the same.
   auto sync = [&] {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(kWaitVm<C::CPW>);
+    lds_barrier();
   };
 
-  // prologue: tiles kt0 and kt0 + 1
+  // prologue: tiles kt0 .. kt0 + 2 in flight, the first two must land
   issue(kt0);
-  if (kt0 < kt1) issue(kt0 + 1);
+  issue(kt0 + 1);
+  issue(kt0 + 2);
   sync();
   f32x16 sc, dpc, sn, dpn;
   if (wkt0 == kt0) sdp(kt0, sc, dpc);
@@ -255,11 +264,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const int mlim = (window > 0 && wq_hi - window >= 0) ? (wq_hi - window) / C::BN + 1 : 0;
   int kt = kt0;
   for (; kt < min(wkt0 - 1, kt1 + 1); ++kt) {
-    if (kt + 2 <= kt1) issue(kt + 2);
+    issue(kt + C::AHEAD);
     sync();
   }
   if (wkt0 > kt0 && kt == wkt0 - 1) {
-    if (kt + 2 <= kt1) issue(kt + 2);
+    issue(kt + C::AHEAD);
     sdp(kt + 1, sc, dpc);
     sync();
     ++kt;
@@ -291,9 +300,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     ++kt;
   }
   for (; kt <= kt1; ++kt) {
-    if (kt + 2 <= kt1) issue(kt + 2);
+    issue(kt + C::AHEAD);
     sync();
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm<0>);  // no copy into LDS outlives the workgroup
 
   if (my_q < T) {
     uint16_t *dqr = dq + base + (size_t)my_q * rs;
