@@ -88,21 +88,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // query qq sees key my_k iff 0 <= qq - my_k <= wm1
   const unsigned wm1 = window > 0 ? (unsigned)(window - 1) : 0x7fffffffu;
 
-  // K and V rows of the wave's keys (B operands), rows past T read as zero
+  // K and V rows of the wave's keys (B operands), rows past T read as zero; loaded
+  // in the prologue, between the tile copies
   bf16x8 kr[C::KST], vr[C::KST];
-  {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)T * rs * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)T * rs * 2);
-#pragma unroll
-    for (int st = 0; st < C::KST; ++st) {
-      const uint32_t off = (my_k * rs + 16 * st + 8 * h) * 2;
-      kr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-      vr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
-    }
-    // landed before any tile copy is issued: later waits then only count copies
-    __builtin_amdgcn_s_waitcnt(kWaitVm<0>);
-    __builtin_amdgcn_sched_barrier(0);
-  }
   f32x16 dka[C::NDB], dva[C::NDB];
 #pragma unroll
   for (int d = 0; d < C::NDB; ++d) {
@@ -372,8 +360,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     }
   };
 
-  // prologue: tiles qt0 .. qt0 + AHEAD - 1 in flight; those up to qt0 + 3 must land
-  for (int t = qt0; t < qt0 + C::AHEAD; ++t) issue(t);
+  // prologue: tiles qt0 .. qt0 + AHEAD - 1 in flight; those up to qt0 + 3 must land.
+  // The K / V row loads go between the copies of tiles qt0 + 3 and qt0 + 4, so all
+  // these memory latencies overlap and one wait covers the rows and the first four
+  // tiles (vector-memory operations complete in order).
+  for (int t = qt0; t < qt0 + 4; ++t) issue(t);
+  {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)T * rs * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)T * rs * 2);
+#pragma unroll
+    for (int st = 0; st < C::KST; ++st) {
+      const uint32_t off = (my_k * rs + 16 * st + 8 * h) * 2;
+      kr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      vr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    }
+  }
+  static_assert(C::AHEAD == 6, "the prologue issues tiles qt0 + 4 and qt0 + 5 last");
+  issue(qt0 + 4);
+  issue(qt0 + 5);
   __builtin_amdgcn_s_waitcnt(kWaitVm<2 * C::NCOPY>);
   lds_barrier();
 
