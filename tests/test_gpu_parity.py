@@ -102,6 +102,32 @@ def test_bf16_raw_normal_qk():
         compare_all(*run_entry_points(x, W, scale), torch.bfloat16)
 
 
+def test_bf16_attention_sink():
+    """Every query puts most of its weight on key 0 (q = q + 6u, k[0] = 20u for a unit
+    u; dO scaled by 0.05 so that |dV| stays below 4): the tiles of key 0 hold P of
+    0.25 to 1 far from the diagonal, so the dK/dV pass takes its hi + lo path for P
+    there and the single-bf16 path elsewhere in the same launch.
+
+    Only the stage-isolated comparison is made (the backward gets the oracle's o and
+    LSE).  On this input dP - delta cancels to a few percent of dP for every query,
+    so the bf16 rounding of the forward's o (through delta = dO . o) moves dq by
+    ~2% relative L2 against the exact gradient, whatever the kernels do."""
+    x = inputs.training_inputs(1, 512, 2, 128, "bf16", seed=23, qk_norm=True)
+    u = torch.randn(128, generator=torch.Generator().manual_seed(5), dtype=torch.float64)
+    u = (u / u.norm()).to(torch.float32)
+    q = x["q"].float() + 6.0 * u
+    k = x["k"].float()
+    k[:, 0] = 20.0 * u
+    x = {"q": q.to(torch.bfloat16), "k": k.to(torch.bfloat16), "v": x["v"],
+         "do": (x["do"].float() * 0.05).to(torch.bfloat16)}
+    scale = 1 / math.sqrt(128)
+    qa, ka = inputs.to_f64(x["q"]), inputs.to_f64(x["k"])
+    for hh in range(2):  # large P on key 0, also far from the diagonal
+        p, _ = orc.head_probs(qa[0, :, hh], ka[0, :, hh], -1, scale)
+        assert p[32:, 0].min() > 0.1
+    compare_all(*run_entry_points(x, -1, scale), torch.bfloat16)
+
+
 def test_long_sequence_sampled():
     """T = 8192, one head, full causal and a 512 window (largest shape tested)."""
     x = inputs.training_inputs(1, 8192, 1, 128, "bf16", seed=3, qk_norm=True)
