@@ -148,19 +148,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   // offset goes into the lane offsets, and offsets from row T on read as zero.
   const int my_tensor = (w * C::CPW) / C::HALF;  // every copy of a wave is K (0) or V (1)
   const __amdgpu_buffer_rsrc_t rsrc_t = make_rsrc(my_tensor ? vb : kb, (uint32_t)T * rs * 2);
-  auto issue = [&](int kt) {
-    const int slot = kt & (C::NSLOT - 1);
+  auto issue_to = [&](int kt, uint16_t *tile) {
     const uint32_t roff = (uint32_t)(kt * C::BN) * (uint32_t)rs * 2;
 #pragma unroll
     for (int cc = 0; cc < C::CPW; ++cc) {
       const int jj = (w * C::CPW + cc) % C::HALF;
       const int db = jj / C::RG, row16 = 16 * (jj % C::RG);
-      buf_copy16_to_lds(rsrc_t,
-                        smem + (2 * slot + my_tensor) * C::TSZ + db * (C::BN * 32) + row16 * 32,
+      buf_copy16_to_lds(rsrc_t, tile + my_tensor * C::TSZ + db * (C::BN * 32) + row16 * 32,
                         lane_off + (uint32_t)(row16 * rs + 32 * db) * 2 + roff);
     }
   };
   auto k_tile = [&](int kt) { return smem + 2 * (kt & (C::NSLOT - 1)) * C::TSZ; };
+  auto issue = [&](int kt) { issue_to(kt, k_tile(kt)); };
 
   // S^T = K Q^T and dP^T = V dO^T of a tile, one query per lane: register i of half
   // h holds key c_row(i, h) of the tile.
@@ -191,15 +190,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   };
   // dQ^T += K^T dS^T for a tile (K^T by one asm block of transposed reads, so the
   // copies in flight are not waited for)
-  auto dq_mfma = [&](int kt, const f32x16 &ds) {
-    bf16x8 kt_op[2][C::NDB];
-    dt_read_tr_perm_block<C::BN, C::NDB>(k_tile(kt), 0, lane, kt_op);
+  auto dq_from = [&](const bf16x8 (&kt_op)[2][C::NDB], const f32x16 &ds) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const bf16x8 dsb = to_bf16x8(ds, 8 * t);
 #pragma unroll
       for (int d = 0; d < C::NDB; ++d) acc[d] = mfma32(kt_op[t][d], dsb, acc[d]);
     }
+  };
+  auto dq_mfma = [&](int kt, const f32x16 &ds) {
+    bf16x8 kt_op[2][C::NDB];
+    dt_read_tr_perm_block<C::BN, C::NDB>(k_tile(kt), 0, lane, kt_op);
+    dq_from(kt_op, ds);
   };
   auto pin = [](float x) {
     asm volatile("" ::"v"(x));
@@ -208,10 +210,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
 
   // One pipeline step for tile kt (S^T, dP^T in sc, dpc): the copies of tile kt + 3
   // start first; the S / dP MFMAs of tile kt + 1 are issued one pair at a time
-  // between the slices of tile kt's dS work, then dQ += dS K for tile kt.
-  auto step = [&](auto mask_tag, int kt, f32x16 &sc, f32x16 &dpc, f32x16 &sn, f32x16 &dpn) {
-    issue(kt + C::AHEAD);
-    const uint16_t *Kn = k_tile(kt + 1), *Vn = Kn + C::TSZ;
+  // between the slices of tile kt's dS work, the last slices also read tile kt's
+  // K^T operands, then dQ += dS K for tile kt.  The tiles come in as distinct
+  // restrict pointers: the compiler then knows the reads do not touch the tile
+  // being copied and does not make them wait for the copies in flight.
+  auto step_body = [&](auto mask_tag, int kt, f32x16 &sc, f32x16 &dpc, f32x16 &sn,
+                       f32x16 &dpn, const uint16_t *__restrict__ Kc,
+                       const uint16_t *__restrict__ Kn, uint16_t *__restrict__ dma)
+                       __attribute__((always_inline)) {
+    issue_to(kt + C::AHEAD, dma);
+    const uint16_t *Vn = Kn + C::TSZ;
     // operands are read AHEAD slices before their MFMAs
     constexpr int AHEAD = 2;
     bf16x8 ka[C::KST], va[C::KST];
@@ -224,16 +232,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);
     const int rel0 = my_q - kt * C::BN - 8 * h;
     constexpr int EPS = 16 / C::KST;  // elements per slice
+    bf16x8 kt_op[2][C::NDB];
+    constexpr int TR0 = C::KST / 2;  // first slice with K^T reads (two operands each)
 #pragma unroll
     for (int st = 0; st < C::KST; ++st) {
       if (st + AHEAD < C::KST) read_ops(st + AHEAD);
+      if (st >= TR0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int kk = 2 * (st - TR0) + u;
+          kt_op[kk / C::NDB][kk % C::NDB] = dt_read_tr_perm<C::BN>(Kc, 16 * (kk / C::NDB),
+                                                                   kk % C::NDB, lane);
+        }
+      }
       sn = mfma32(ka[st], qr[st], st ? sn : f32x16{});
       dpn = mfma32(va[st], gr[st], st ? dpn : f32x16{});
       __builtin_amdgcn_sched_barrier(0);
       ds_elems(mask_tag, sc, dpc, rel0, EPS * st, EPS);
       pin(dpc[EPS * st + EPS - 1]);
     }
-    dq_mfma(kt, dpc);
+    dq_from(kt_op, dpc);
+  };
+  auto step = [&](auto mask_tag, int kt, f32x16 &sc, f32x16 &dpc, f32x16 &sn, f32x16 &dpn)
+      __attribute__((always_inline)) {
+    step_body(mask_tag, kt, sc, dpc, sn, dpn, k_tile(kt), k_tile(kt + 1), k_tile(kt + C::AHEAD));
   };
   auto last_step = [&](int kt, f32x16 &sc, f32x16 &dpc) {
     issue(kt + C::AHEAD);
