@@ -282,8 +282,11 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # ~0.3 ms per step: the defaults give the GPU ~0.3 s of load before timing (it
+    # reaches its steady clocks after a few hundred milliseconds; 10 warm-up steps
+    # measured 10% slower) and time ~0.6 s
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--config", default="small", help="training workload (default: small)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
