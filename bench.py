@@ -4,9 +4,12 @@
 A step is one forward + backward of causal attention on the "small" training
 workload (B8 H6 T2048 D128, bf16, full causal; seeded synthetic data), issued as
 the library's three kernels in order (forward; dQ pass, which also computes
-delta; dK/dV pass), exactly what swattn_fwd + swattn_bwd launch.  ``value`` is window-masked TFLOP/s of the whole step: forward
-4*D*N_vis*B*H, backward 2.5x that (the usual five-product accounting), with
-N_vis = sum_i min(i+1, W) visible (query, key) pairs per head.
+delta; dK/dV pass), exactly what swattn_fwd + swattn_bwd launch.  ``--config``
+picks another training workload; one with several windows (mid-alt: 512, 2048,
+512, 2048) runs that many layers per step, forwards first, then backwards in
+reverse order.  ``value`` is window-masked TFLOP/s of the whole step: forward
+4*D*N_vis*B*H per layer, backward 2.5x that (the usual five-product
+accounting), with N_vis = sum_i min(i+1, W) visible (query, key) pairs per head.
 
 Also measured in the same run:
 * per-kernel average durations from HIP events recorded on the stream the
@@ -74,6 +77,15 @@ def train_accounting(B, H, T, D, W, elem=2):
     }
 
 
+def step_accounting(B, H, T, D, windows):
+    """train_accounting summed over the layers of one step (one layer per window)."""
+    per = [train_accounting(B, H, T, D, W) for W in windows]
+    out = {k: sum(a[k] for a in per) for k in ("pairs", "flops_fwd", "flops_bwd")}
+    for k in ("kernel_flops", "kernel_bytes"):
+        out[k] = {n: sum(a[k][n] for a in per) for n in per[0][k]}
+    return out
+
+
 def decode_bytes(lengths, H, D, W, elem=2):
     vis = sum(min(int(L), W) if W > 0 else int(L) for L in lengths)
     B = len(lengths)
@@ -90,54 +102,73 @@ def source_hash() -> str:
 
 # ----------------------------------------------------------------------------- GPU legs
 def bench_training(torch, swattn, inputs, cfg_name, steps, warmup):
+    """Times `steps` training steps of workload `cfg_name`.  A step runs every layer of the
+    workload's window schedule (one layer per entry of its `windows`, each with its own
+    seeded inputs): the forwards in layer order, then the backwards in reverse order, as a
+    model's training step issues them."""
     c = inputs.CONFIGS[cfg_name]
-    B, H, T, D, W = c["B"], c["H"], c["T"], c["D"], c["windows"][0]
+    B, H, T, D = c["B"], c["H"], c["T"], c["D"]
+    windows = list(c["windows"])
     scale = 1.0 / math.sqrt(D)
-    x = {n: t.to("cuda:0") for n, t in inputs.config_inputs(cfg_name).items()}
-    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda:0")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(swattn.swattn_bwd_workspace_size(B, H, T, D), dtype=torch.uint8, device="cuda:0")
     lib = swattn.lib()
     P = swattn._ptr
     stream = torch.cuda.current_stream()
     sh = swattn.ctypes.c_void_p(stream.cuda_stream)
+    ws = torch.empty(swattn.swattn_bwd_workspace_size(B, H, T, D), dtype=torch.uint8, device="cuda:0")
+    layers = []
+    for i, W in enumerate(windows):
+        x = {n: t.to("cuda:0") for n, t in inputs.config_inputs(cfg_name, layer=i).items()}
+        q = x["q"]
+        layers.append(dict(W=W, q=q, k=x["k"], v=x["v"], do=x["do"], o=torch.empty_like(q),
+                           lse=torch.empty((B, H, T), dtype=torch.float32, device="cuda:0"),
+                           dq=torch.empty_like(q), dk=torch.empty_like(q), dv=torch.empty_like(q)))
 
     def check(rc, what):
         if rc != 0:
             raise RuntimeError(f"{what}: {swattn.status_string(rc)}")
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        check(lib.swattn_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, T, D, W, scale, sh), "fwd")
-        if ev is not None:
-            ev[1].record(stream)
-        # swattn_bwd is exactly these two passes; the dQ pass also writes delta
-        check(lib.swattn_bwd_dq(P(q), P(k), P(v), P(o), P(do), P(lse), P(ws), P(dq), B, H, T, D, W,
-                                scale, sh), "bwd_dq")
-        if ev is not None:
-            ev[2].record(stream)
-        check(lib.swattn_bwd_dkdv(P(q), P(k), P(v), P(do), P(lse), P(ws), P(dk), P(dv), B, H, T, D,
-                                  W, scale, sh), "bwd_dkdv")
-        if ev is not None:
-            ev[3].record(stream)
+        # ev[i] holds four events per layer: before forward, forward | dQ, dQ | dK/dV, after
+        for i, L in enumerate(layers):
+            if ev is not None:
+                ev[i][0].record(stream)
+            check(lib.swattn_fwd(P(L["q"]), P(L["k"]), P(L["v"]), P(L["o"]), P(L["lse"]), B, H, T,
+                                 D, L["W"], scale, sh), "fwd")
+            if ev is not None:
+                ev[i][1].record(stream)
+        for i in reversed(range(len(layers))):
+            L = layers[i]
+            if ev is not None:
+                ev[i][2].record(stream)
+            # swattn_bwd is exactly these two passes; the dQ pass also writes delta
+            check(lib.swattn_bwd_dq(P(L["q"]), P(L["k"]), P(L["v"]), P(L["o"]), P(L["do"]),
+                                    P(L["lse"]), P(ws), P(L["dq"]), B, H, T, D, L["W"], scale, sh),
+                  "bwd_dq")
+            if ev is not None:
+                ev[i][3].record(stream)
+            check(lib.swattn_bwd_dkdv(P(L["q"]), P(L["k"]), P(L["v"]), P(L["do"]), P(L["lse"]),
+                                      P(ws), P(L["dk"]), P(L["dv"]), B, H, T, D, L["W"], scale, sh),
+                  "bwd_dkdv")
+            if ev is not None:
+                ev[i][4].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in layers]
+           for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    names = ["fwd", "bwd_dq", "bwd_dkdv"]
-    per = {n: statistics.fmean(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
-    return {"B": B, "H": H, "T": T, "D": D, "W": W, "wall_s": wall, "kernel_ms": per,
-            "acct": train_accounting(B, H, T, D, W)}
+    spans = {"fwd": (0, 1), "bwd_dq": (2, 3), "bwd_dkdv": (3, 4)}
+    # per-kernel time of one step: summed over the layers, averaged over the steps
+    per = {n: statistics.fmean(sum(e[i][a].elapsed_time(e[i][b]) for i in range(len(layers)))
+                               for e in evs) for n, (a, b) in spans.items()}
+    return {"B": B, "H": H, "T": T, "D": D, "windows": windows, "wall_s": wall, "kernel_ms": per,
+            "acct": step_accounting(B, H, T, D, windows)}
 
 
 def bench_decode(torch, swattn, inputs, iters):
@@ -347,15 +378,18 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), RMS-normalised q/k)",
         "config": {"workload": f"{args.config}: B{tr['B']} H{tr['H']} T{tr['T']} D{tr['D']} "
-                               f"window {tr['W']} bf16, forward + backward",
-                   "B": tr["B"], "H": tr["H"], "T": tr["T"], "D": tr["D"], "window": tr["W"],
+                               f"bf16, {len(tr['windows'])} layer(s), windows {tr['windows']} "
+                               f"(-1 = full causal), forward + backward",
+                   "B": tr["B"], "H": tr["H"], "T": tr["T"], "D": tr["D"],
+                   "windows": tr["windows"],
                    "parallelism": "none (1 GPU)"},
         "pct_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "kernels": kernels,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_for(dom),
+                     # stored counters are taken on the default (small) workload
+                     "traffic": traffic_for(dom) if args.config == "small" else None,
                      "algorithmic_bytes": acct["kernel_bytes"][dom]},
     }
     if not args.no_decode:
