@@ -36,6 +36,10 @@ HIPCC_FLAGS = [
 # its accumulators in AGPRs, leaving the arch VGPRs to its operands.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 EXTRA_FLAGS = {s: VGPR_FORM for s in SOURCES if s != "dkdv_bf16.hip"}
+# The forward's row maxima are taken over MFMA results, which are never NaN.  Without
+# this flag every fmaxf operand is first quieted (one extra v_max per element) and the
+# three-input v_max3 is not formed.
+EXTRA_FLAGS["fwd_bf16.hip"] = VGPR_FORM + ["-fno-honor-nans"]
 
 
 def hipcc() -> str:

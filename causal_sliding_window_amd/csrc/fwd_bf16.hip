@@ -18,7 +18,9 @@
 //   * the running max is only moved (and O rescaled) when a row max grows by
 //     more than 2^8 in exp2 units, which keeps every P below 256;
 //   * the element mask runs only on tiles crossing the diagonal or the window's
-//     lower edge.
+//     lower edge;
+//   * the unmasked loop is aligned so that its two steps always use the same LDS
+//     slots: every operand address is then a lane offset plus a constant.
 #include <type_traits>
 
 #include "common.h"
@@ -303,11 +305,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   }
   // unmasked tiles, two per iteration: S of the next tile alternates between sc and
   // sn, so no registers are copied
-  for (; kt + 1 < wkt1; kt += 2) {
+  if (kt + 1 < wkt1 && ((kt - kt0) & 1)) {  // align the pair loop to slot 0
     step(std::false_type{}, [&] { loads(kt); }, k_next(kt), v_cur(kt), kt * C::BN, sc, sn);
+    sc = sn;
     sync();
-    step(std::false_type{}, [&] { loads(kt + 1); }, k_next(kt + 1), v_cur(kt + 1),
-         (kt + 1) * C::BN, sn, sc);
+    ++kt;
+  }
+  // (kt - kt0) is even here: the slots of both steps are fixed, so every LDS address
+  // is a loop-invariant lane offset plus a constant
+  for (; kt + 1 < wkt1; kt += 2) {
+    step(std::false_type{}, [&] { loads(kt); }, smem + 2 * C::TSZ, smem + C::TSZ, kt * C::BN, sc,
+         sn);
+    sync();
+    step(std::false_type{}, [&] { loads(kt + 1); }, smem, smem + 3 * C::TSZ, (kt + 1) * C::BN, sn,
+         sc);
     sync();
   }
   if (kt < wkt1) {
