@@ -171,17 +171,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   }
 }
 
-// One workgroup per (b, h) with more than one chunk.  Pass 1: every thread takes
-// chunks tid, tid + 256, ... for the maximum and the sum of exp(lse_c - max).  Pass
-// 2: thread (g, d) accumulates chunks g, g + G, ... of column d (G = 256 / D), with
-// its loads unrolled so they are in flight together; the G sums are added in a
-// fixed order, so the result does not depend on timing.
+// One workgroup per (b, h) with more than one chunk.  Thread (g, d) (G = 256 / D
+// groups) takes chunks g, g + G, ... of column d.  Each batch of up to MB of its
+// chunks is loaded at once, partial o and lse together, before any is used, so a
+// batch costs one memory latency; the maximum over all chunks' lse (thread tid
+// loads chunks tid, tid + 256, ... with the first batch) is reduced in between.  The
+// G column sums are added in a fixed order: the result does not depend on timing.
 template <typename TT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float *__restrict__ ws_o, const float *__restrict__ ws_lse,
     const int *__restrict__ seqlens, TT *__restrict__ o, float *__restrict__ lse, int H, int Tmax,
     int window, int nsplit) {
   constexpr int G = 256 / D;
+  constexpr int MB = 16;  // chunks per thread and batch
   __shared__ float red[4];
   __shared__ float part[G][D];
   const int bh = blockIdx.x, b = bh / H;
@@ -191,8 +193,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int nch = (n + kDecodeChunk - 1) / kDecodeChunk;
   if (nch <= 1) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = tid / D, d = tid % D;
   const float *ls = ws_lse + (size_t)bh * nsplit;
+  const float *os = ws_o + (size_t)bh * nsplit * D + d;
 
+  // first batch of this thread's chunks, and its share of the lse maximum
+  float lv[MB], ov[MB];
+#pragma unroll
+  for (int u = 0; u < MB; ++u) {
+    const int cc = g + u * G;
+    lv[u] = cc < nch ? ls[cc] : -INFINITY;
+    ov[u] = cc < nch ? os[(size_t)cc * D] : 0.f;
+  }
   float m = -INFINITY;
   for (int cc = tid; cc < nch; cc += 256) m = fmaxf(m, ls[cc]);
 #pragma unroll
@@ -200,33 +212,39 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   if (lane == 0) red[w] = m;
   __syncthreads();
   const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float s = 0.f;
-  for (int cc = tid; cc < nch; cc += 256) s += expf(ls[cc] - M);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (lane == 0) red[w] = s;
-  __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
 
-  const int g = tid / D, d = tid % D;
-  const float *os = ws_o + (size_t)bh * nsplit * D + d;
-  float acc = 0.f;
-  int cc = g;
-  for (; cc + 7 * G < nch; cc += 8 * G) {
-    float lv[8], ov[8];
+  // sum of exp(lse_c - M) over the chunks of column 0 of each group (every chunk
+  // once), and this thread's o accumulation
+  float acc = 0.f, s = 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      lv[u] = ls[cc + u * G];
-      ov[u] = os[(size_t)(cc + u * G) * D];
+  for (int u = 0; u < MB; ++u) {
+    const float e = expf(lv[u] - M);  // 0 for chunks past nch
+    acc = fmaf(e, ov[u], acc);
+    s += e;
+  }
+  for (int c0 = G * MB; c0 < nch; c0 += G * MB) {  // later batches (more than G*MB chunks)
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const int cc = c0 + g + u * G;
+      lv[u] = cc < nch ? ls[cc] : -INFINITY;
+      ov[u] = cc < nch ? os[(size_t)cc * D] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc = fmaf(expf(lv[u] - M), ov[u], acc);
+    for (int u = 0; u < MB; ++u) {
+      const float e = expf(lv[u] - M);
+      acc = fmaf(e, ov[u], acc);
+      s += e;
+    }
   }
-  for (; cc < nch; cc += G) acc = fmaf(expf(ls[cc] - M), os[(size_t)cc * D], acc);
   part[g][d] = acc;
+  __syncthreads();  // red[] is read above by every thread before it is reused below
+  // total: the G groups of column 0 cover every chunk once
+  if (d == 0) red[g] = s;
   __syncthreads();
   if (tid < D) {
+    float tot = red[0];
+#pragma unroll
+    for (int i = 1; i < G; ++i) tot += red[i];
     float a = part[0][tid];
 #pragma unroll
     for (int i = 1; i < G; ++i) a += part[i][tid];

@@ -202,6 +202,24 @@ def test_decode_shapes(dtype, D, W):
     check("lse", lse, rl, td, lse=True)
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("W", [-1, 9000])
+def test_decode_long_cache(dtype, D, W):
+    """Caches of 20000 rows: up to 157 chunks of 128 rows per sequence, so the merge
+    runs several batches of chunks per thread (D = 128: 32 chunks per batch; D = 64:
+    64)."""
+    lens = [20000, 9001, 4097]
+    d = inputs.decode_inputs(len(lens), 2, D, 20000, dtype, seed=11, lengths=lens)
+    g = _gpu(d)
+    scale = 1 / math.sqrt(D)
+    o, lse = swattn.decode(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], W, scale)
+    torch.cuda.synchronize()
+    ro, rl = _decode_oracle(d, W, scale)
+    td = inputs.DTYPES[dtype]
+    check("o", o, ro, td)
+    check("lse", lse, rl, td, lse=True)
+
+
 def test_decode_clamps_and_empty():
     """seqlens above Tmax is clamped to Tmax; seqlens 0 gives o = 0, lse = -inf."""
     d = inputs.decode_inputs(3, 2, 128, 300, "bf16", seed=1, lengths=[0, 300, 300])
