@@ -14,6 +14,10 @@ accounting), with N_vis = sum_i min(i+1, W) visible (query, key) pairs per head.
 Also measured in the same run:
 * per-kernel average durations from HIP events recorded on the stream the
   kernels run on, and the roofline of the dominant kernel;
+* the same step cold (median of 50, each after a 1 GiB fill) and under the
+  12*D*N_vis model-FLOP count;
+* a 1 GiB device copy and an 8192^3 bf16 GEMM (torch) as measured ceilings next
+  to the published peaks;
 * KV-cache decode (32 sequences, H12 D128 bf16, lengths 512..4096 from seed 7;
   full causal and window 1024) in HBM GB/s, cold cache (a 1 GiB buffer is
   written before every timed call so the 256 MB MALL holds none of the cache);
@@ -101,7 +105,7 @@ def source_hash() -> str:
 
 
 # ----------------------------------------------------------------------------- GPU legs
-def bench_training(torch, swattn, inputs, cfg_name, steps, warmup):
+def bench_training(torch, swattn, inputs, cfg_name, steps, warmup, cold_steps=50):
     """Times `steps` training steps of workload `cfg_name`.  A step runs every layer of the
     workload's window schedule (one layer per entry of its `windows`, each with its own
     seeded inputs): the forwards in layer order, then the backwards in reverse order, as a
@@ -163,11 +167,24 @@ def bench_training(torch, swattn, inputs, cfg_name, steps, warmup):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # cold: a 1 GiB fill before each step, so the 256 MB MALL holds none of the inputs
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+    cold = []
+    for _ in range(cold_steps):
+        flush.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
     spans = {"fwd": (0, 1), "bwd_dq": (2, 3), "bwd_dkdv": (3, 4)}
     # per-kernel time of one step: summed over the layers, averaged over the steps
     per = {n: statistics.fmean(sum(e[i][a].elapsed_time(e[i][b]) for i in range(len(layers)))
                                for e in evs) for n, (a, b) in spans.items()}
     return {"B": B, "H": H, "T": T, "D": D, "windows": windows, "wall_s": wall, "kernel_ms": per,
+            "cold_ms": statistics.median(cold) if cold else None,
             "acct": step_accounting(B, H, T, D, windows)}
 
 
@@ -218,38 +235,93 @@ def bench_decode(torch, swattn, inputs, iters):
     return out
 
 
+def measured_refs(torch):
+    """Practical ceilings measured on this GPU, reported next to the published peaks: a
+    1 GiB device copy (read + write bytes) and an 8192^3 bf16 GEMM (torch.matmul)."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fn, n=10):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(n):
+            a, b = ev(), ev()
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return statistics.median(ts)
+
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    del src, dst
+    m = 8192
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(0)
+    x = torch.randn(m, m, device="cuda:0", generator=g).to(torch.bfloat16)
+    y = torch.randn(m, m, device="cuda:0", generator=g).to(torch.bfloat16)
+    t_mm = timed(lambda: torch.matmul(x, y))
+    del x, y
+    return {"copy_GB_per_s": round(2 * n * 4 / t_copy / 1e9, 1),
+            "gemm_bf16_TFLOP_per_s": round(2 * m ** 3 / t_mm / 1e12, 1),
+            "what": "1 GiB device copy (read + write bytes); 8192^3 bf16 torch.matmul"}
+
+
 # ----------------------------------------------------------------------------- CPU oracle leg
 def cpu_baseline(inputs, budget_s=12.0):
     import numpy as np
     from oracle import attention as orc
+    threads, blas = 1, "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            threads = max(i.get("num_threads", 1) for i in libs)
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in libs)
     except Exception:  # pragma: no cover
-        threads = 1
+        pass
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
     c = inputs.CONFIGS["small"]
     B, H, T, D, W = c["B"], c["H"], c["T"], c["D"], c["windows"][0]
     x = inputs.config_inputs("small")
     a = {n: inputs.to_f64(t) for n, t in x.items()}
     scale = 1.0 / math.sqrt(D)
-    done, flops = 0, 0
+    done, t_f, t_b = 0, 0.0, 0.0
+    pairs = visible_pairs(T, W)
     t0 = time.perf_counter()
     for b in range(B):
         for h in range(H):
+            t1 = time.perf_counter()
             orc.head_fwd(a["q"][b, :, h], a["k"][b, :, h], a["v"][b, :, h], W, scale)
+            t2 = time.perf_counter()
             orc.head_bwd(a["q"][b, :, h], a["k"][b, :, h], a["v"][b, :, h], a["do"][b, :, h], W, scale)
+            t3 = time.perf_counter()
+            t_f, t_b = t_f + (t2 - t1), t_b + (t3 - t2)
             done += 1
-            flops += 14 * D * visible_pairs(T, W)
-            if time.perf_counter() - t0 > budget_s:
+            if t3 - t0 > budget_s:
                 break
         else:
             continue
         break
-    el = time.perf_counter() - t0
-    return {"value": round(flops / el / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+    el = t_f + t_b
+    return {"value": round(14 * D * pairs * done / el / 1e12, 5), "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "fwd_TFLOP_per_s": round(4 * D * pairs * done / t_f / 1e12, 5),
+            "bwd_TFLOP_per_s": round(10 * D * pairs * done / t_b / 1e12, 5),
+            "cpu": cpu, "blas": blas,
             "sample": f"{done} of {B * H} heads of the small workload (T={T}, D={D}, full causal): "
-                      f"NumPy fp64 oracle forward + backward, {el:.1f} s, same masked-FLOP count"}
+                      f"NumPy fp64 oracle forward ({t_f:.1f} s) + backward ({t_b:.1f} s), "
+                      f"same masked-FLOP count"}
 
 
 # ----------------------------------------------------------------------------- counters
@@ -321,6 +393,8 @@ def main():
     ap.add_argument("--config", default="small", help="training workload (default: small)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-refs", action="store_true",
+                    help="skip the measured copy-bandwidth and GEMM references")
     ap.add_argument("--decode-iters", type=int, default=20)
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="also run one torch copy of this many bytes (counter calibration)")
@@ -362,7 +436,9 @@ def main():
     dom = max(tr["kernel_ms"], key=lambda n: tr["kernel_ms"][n])
     dom_ms = tr["kernel_ms"][dom]
     achieved = acct["kernel_flops"][dom] / (dom_ms * 1e-3) / 1e12
-    log(f"step {ms_step:.3f} ms, {value:.1f} TFLOP/s; kernels {kernels}")
+    model_tflops = 12 * tr["D"] * acct["pairs"] / (ms_step * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms (cold {tr['cold_ms']:.3f} ms), {value:.1f} TFLOP/s; "
+        f"kernels {kernels}")
 
     res = {
         "metric": METRIC,
@@ -384,6 +460,10 @@ def main():
                    "windows": tr["windows"],
                    "parallelism": "none (1 GPU)"},
         "pct_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        # the same step under the 12*D*N_vis "model FLOP" count (no recompute of S)
+        "model_TFLOP_per_s": round(model_tflops, 2),
+        # median of 50 steps, each after a 1 GiB fill (inputs not in the MALL)
+        "cold_ms_per_step": round(tr["cold_ms"], 4),
         "kernels": kernels,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -395,6 +475,13 @@ def main():
     if not args.no_decode:
         res["decode"] = bench_decode(torch, swattn, inputs, args.decode_iters)
         log(f"decode {res['decode']}")
+    if not args.no_refs:
+        refs = measured_refs(torch)
+        res["measured_refs"] = refs
+        res["roofline"]["frac_of_measured_gemm"] = round(achieved / refs["gemm_bf16_TFLOP_per_s"], 4)
+        for d in res.get("decode", {}).values():
+            d["frac_of_measured_copy"] = round(d["GB_per_s"] / refs["copy_GB_per_s"], 4)
+        log(f"measured refs {refs}")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inputs)
         log(f"cpu baseline {res['cpu_baseline']}")
