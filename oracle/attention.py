@@ -28,6 +28,12 @@ Readings where the pages are silent:
   q, k, v (LSE is an output only; nothing flows back through it).
 * Decode: ``seqlens[b] = L`` counts valid cache rows including the new token; the
   query sits at position ``L - 1``.  ``L == 0`` gives o = 0, LSE = -inf.
+* Grouped-query attention (same guide, section 1 feature list: fewer K/V heads than
+  query heads, for faster inference; the multi-query case, one K/V head, is in the
+  architecture list of the release article).  The pages do not say which query
+  heads share a K/V head; the reading here is contiguous groups: with H query heads
+  and Hkv K/V heads (H a multiple of Hkv), query head h uses K/V head h // (H / Hkv).
+  Its gradients with respect to k and v are the sums over the group's query heads.
 
 Every array is float64.  No blocking, fusion or reordering: each function is the
 definition, written out with NumPy matrix products as its only library steps.
@@ -130,6 +136,14 @@ def head_bwd(q, k, v, do, window: int, scale: float, o=None):
     return dq, dk, dv
 
 
+def _group(H: int, k) -> int:
+    """Query heads per K/V head (1 without grouping), from k's head count."""
+    Hkv = np.shape(k)[2]
+    if Hkv <= 0 or H % Hkv:
+        raise ValueError(f"{H} query heads cannot be grouped over {Hkv} K/V heads")
+    return H // Hkv
+
+
 def _heads(B: int, H: int, heads):
     if heads is None:
         return [(b, h) for b in range(B) for h in range(H)]
@@ -137,33 +151,44 @@ def _heads(B: int, H: int, heads):
 
 
 def attn_fwd(q, k, v, window: int, scale: float, heads=None):
-    """Forward over [B, T, H, D] arrays.
+    """Forward over q [B, T, H, D] and k, v [B, T, Hkv, D] (Hkv = H, or a divisor
+    of H for grouped-query attention: query head h reads K/V head h // (H / Hkv)).
 
     Returns (o [B, T, H, D], lse [B, H, T]).  With ``heads`` (a list of (b, h))
     only those heads are computed; the others are left NaN.
     """
     q = np.asarray(q, dtype=np.float64)
     B, T, H, D = q.shape
+    G = _group(H, k)
     o = np.full((B, T, H, D), np.nan)
     lse = np.full((B, H, T), np.nan)
     for b, h in _heads(B, H, heads):
-        o[b, :, h, :], lse[b, h, :] = head_fwd(q[b, :, h, :], k[b, :, h, :],
-                                               v[b, :, h, :], window, scale)
+        o[b, :, h, :], lse[b, h, :] = head_fwd(q[b, :, h, :], k[b, :, h // G, :],
+                                               v[b, :, h // G, :], window, scale)
     return o, lse
 
 
 def attn_bwd(q, k, v, do, window: int, scale: float, heads=None, o=None):
-    """Backward over [B, T, H, D] arrays -> (dq, dk, dv); see :func:`head_bwd`
-    (``o``, optional [B, T, H, D]: the forward output delta is taken from)."""
+    """Backward over q, do [B, T, H, D] and k, v [B, T, Hkv, D] -> (dq [B, T, H, D],
+    dk, dv [B, T, Hkv, D]); see :func:`head_bwd` (``o``, optional [B, T, H, D]: the
+    forward output delta is taken from).  A K/V head's dk and dv sum the gradients of
+    every query head that reads it; with ``heads``, the sum runs over the listed ones
+    and K/V heads no listed head reads are left NaN."""
     q = np.asarray(q, dtype=np.float64)
     B, T, H, D = q.shape
+    G = _group(H, k)
     dq = np.full((B, T, H, D), np.nan)
-    dk = np.full((B, T, H, D), np.nan)
-    dv = np.full((B, T, H, D), np.nan)
+    dk = np.full((B, T, H // G, D), np.nan)
+    dv = np.full((B, T, H // G, D), np.nan)
     for b, h in _heads(B, H, heads):
-        dq[b, :, h, :], dk[b, :, h, :], dv[b, :, h, :] = head_bwd(
-            q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], do[b, :, h, :],
+        dq[b, :, h, :], gk, gv = head_bwd(
+            q[b, :, h, :], k[b, :, h // G, :], v[b, :, h // G, :], do[b, :, h, :],
             window, scale, None if o is None else o[b, :, h, :])
+        if np.isnan(dk[b, 0, h // G, 0]):
+            dk[b, :, h // G, :] = 0.0
+            dv[b, :, h // G, :] = 0.0
+        dk[b, :, h // G, :] += gk
+        dv[b, :, h // G, :] += gv
     return dq, dk, dv
 
 
@@ -171,7 +196,8 @@ def attn_decode(q, k_cache, v_cache, seqlens, window: int, scale: float,
                 seqs=None):
     """One-token decode against a KV cache (guide section 6, "Inference engine").
 
-    q: [B, H, D]; k_cache, v_cache: [B, Tmax, H, D]; seqlens: [B] ints.
+    q: [B, H, D]; k_cache, v_cache: [B, Tmax, Hkv, D] (query head h reads K/V head
+    h // (H / Hkv)); seqlens: [B] ints.
     Sequence b's query sits at position ``L = seqlens[b]`` minus one and sees the
     cache rows ``0 .. L-1`` that pass :func:`visible_mask`.  Rows ``>= L`` are
     never read.  Returns (o [B, H, D], lse [B, H]); with ``seqs`` only those
@@ -179,6 +205,7 @@ def attn_decode(q, k_cache, v_cache, seqlens, window: int, scale: float,
     """
     q = np.asarray(q, dtype=np.float64)
     B, H, D = q.shape
+    G = _group(H, k_cache)
     Tmax = k_cache.shape[1]
     o = np.full((B, H, D), np.nan)
     lse = np.full((B, H), np.nan)
@@ -191,8 +218,8 @@ def attn_decode(q, k_cache, v_cache, seqlens, window: int, scale: float,
                 o[b, h] = 0.0
                 lse[b, h] = -np.inf
                 continue
-            kb = np.asarray(k_cache[b, :L, h, :], dtype=np.float64)
-            vb = np.asarray(v_cache[b, :L, h, :], dtype=np.float64)
+            kb = np.asarray(k_cache[b, :L, h // G, :], dtype=np.float64)
+            vb = np.asarray(v_cache[b, :L, h // G, :], dtype=np.float64)
             p, l_ = head_probs(q[b, h][None, :], kb, window, scale, q_pos0=L - 1)
             o[b, h] = (p @ vb)[0]
             lse[b, h] = l_[0]

@@ -359,3 +359,78 @@ def test_delta_from_given_output(T, W, D):
     for a, b in zip(got, ref[2:]):
         np.testing.assert_allclose(a, np.array(b), atol=1e-12)
     assert not np.allclose(got[0], orc.head_bwd(q, k, v, do, W, 0.6)[0], atol=1e-9)
+
+
+# ----------------------------------------------------------------------------- grouped K/V heads
+@pytest.mark.parametrize("H,Hkv", [(6, 1), (6, 2), (6, 3), (4, 4)])
+@pytest.mark.parametrize("T,W", [(17, -1), (40, 5)])
+def test_gqa_matches_torch_sdpa_enable_gqa(H, Hkv, T, W):
+    """Grouped-query forward and backward against PyTorch's CPU SDPA in fp64 with
+    enable_gqa (its own head mapping, query head h on K/V head h // (H / Hkv)) and
+    autograd: a wrong group mapping (h % Hkv) or a missing sum over a group fails."""
+    B, D = 2, 8
+    x = {n: RNG.standard_normal((B, T, H if n in ("q", "do") else Hkv, D))
+         for n in ("q", "k", "v", "do")}
+    scale = 1 / math.sqrt(D)
+    o, lse = orc.attn_fwd(x["q"], x["k"], x["v"], W, scale)
+    dq, dk, dv = orc.attn_bwd(x["q"], x["k"], x["v"], x["do"], W, scale)
+    assert dk.shape == (B, T, Hkv, D) and dv.shape == (B, T, Hkv, D)
+    t = {n: torch.tensor(a).permute(0, 2, 1, 3).contiguous().requires_grad_(n != "do")
+         for n, a in x.items()}
+    band = np.tril(np.ones((T, T), bool))
+    if W > 0:
+        band &= np.triu(np.ones((T, T), bool), -(W - 1))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        t["q"], t["k"], t["v"], attn_mask=torch.tensor(band), scale=scale, enable_gqa=True)
+    ref.backward(t["do"])
+    tr = lambda a: a.detach().permute(0, 2, 1, 3).numpy()  # noqa: E731
+    np.testing.assert_allclose(o, tr(ref), atol=1e-12)
+    np.testing.assert_allclose(dq, tr(t["q"].grad), atol=1e-12)
+    np.testing.assert_allclose(dk, tr(t["k"].grad), atol=1e-12)
+    np.testing.assert_allclose(dv, tr(t["v"].grad), atol=1e-12)
+    # lse of each query head against the logsumexp of its own K/V head's logits
+    kv = np.repeat(x["k"], H // Hkv, axis=2)
+    s = scale * np.einsum("bihd,bjhd->bhij", x["q"], kv)
+    s = np.where(band, s, -np.inf)
+    m = s.max(-1, keepdims=True)
+    np.testing.assert_allclose(lse, (m + np.log(np.exp(s - m).sum(-1, keepdims=True)))[..., 0],
+                               atol=1e-12)
+
+
+def test_gqa_finite_differences():
+    """dk and dv of a shared K/V head are the derivatives of L = sum dO . o over all the
+    query heads that read it (central differences, one K/V head shared by three)."""
+    B, T, H, Hkv, D, W = 1, 5, 3, 1, 3, 3
+    q, do = _rand(B, T, H, D), _rand(B, T, H, D)
+    k, v = _rand(B, T, Hkv, D), _rand(B, T, Hkv, D)
+    scale, h = 0.7, 1e-6
+
+    def loss(k_, v_):
+        return float((orc.attn_fwd(q, k_, v_, W, scale)[0] * do).sum())
+
+    _, dk, dv = orc.attn_bwd(q, k, v, do, W, scale)
+    for which, g in ((0, dk), (1, dv)):
+        fd = np.zeros_like(g)
+        for idx in np.ndindex(*g.shape):
+            args_p, args_m = [k.copy(), v.copy()], [k.copy(), v.copy()]
+            args_p[which][idx] += h
+            args_m[which][idx] -= h
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert np.abs(fd - g).max() / max(1.0, np.abs(g).max()) < 1e-6, which
+
+
+@pytest.mark.parametrize("W", [-1, 3])
+def test_gqa_decode_is_last_row_of_forward(W):
+    """Grouped decode reads K/V head h // (H / Hkv), like the grouped forward."""
+    B, T, H, Hkv, D = 2, 9, 4, 2, 5
+    q, k, v = _rand(B, T, H, D), _rand(B, T, Hkv, D), _rand(B, T, Hkv, D)
+    o, lse = orc.attn_fwd(q, k, v, W, 0.5)
+    od, ld = orc.attn_decode(q[:, T - 1], k, v, np.array([T, T]), W, 0.5)
+    np.testing.assert_allclose(od, o[:, T - 1], atol=1e-14)
+    np.testing.assert_allclose(ld, lse[:, :, T - 1], atol=1e-14)
+
+
+def test_gqa_rejects_uneven_groups():
+    q, k = _rand(1, 4, 6, 2), _rand(1, 4, 4, 2)
+    with pytest.raises(ValueError):
+        orc.attn_fwd(q, k, k, -1, 1.0)
