@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 101;  // 0.1.1: swattn_bwd_dq takes o and writes delta
+constexpr int kVersion = 102;  // 0.1.2: grouped-query entry points (*_gqa)
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -24,6 +24,18 @@ int check_common(int B, int H, int T, int D, int window) {
   // buffer loads address one sequence's [T, H, D] block with 32-bit byte offsets
   if ((long long)(T + 128) * H * D * 2 > INT_MAX) return SWATTN_ERR_UNSUPPORTED;
   return SWATTN_OK;
+}
+
+// Hkv K/V heads shared by H query heads in contiguous groups of H / Hkv
+int check_group(int H, int Hkv) {
+  if (Hkv <= 0 || H % Hkv != 0) return SWATTN_ERR_INVALID_ARG;
+  return SWATTN_OK;
+}
+
+// bytes of the delta part of the backward workspace (float32 [B, H, T], 256-aligned)
+size_t delta_bytes(int B, int H, int T) {
+  const size_t bytes = (size_t)B * H * T * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
 }
 
 int all_aligned(std::initializer_list<const void *> ps) {
@@ -54,10 +66,12 @@ hipError_t launch_bwd_pre(bool bf16, const void *o, const void *dO, float *delta
 
 hipError_t launch_bwd_dkdv(bool bf16, const void *q, const void *k, const void *v,
                            const void *dO, const float *lse, const float *delta, void *dk,
-                           void *dv, int B, int H, int T, int D, int window, float scale,
-                           hipStream_t st) {
+                           void *dv, float *part, int B, int H, int Hkv, int T, int D,
+                           int window, float scale, hipStream_t st) {
   if (bf16)
-    return launch_bwd_dkdv_bf16(q, k, v, dO, lse, delta, dk, dv, B, H, T, D, window, scale, st);
+    return launch_bwd_dkdv_bf16(q, k, v, dO, lse, delta, dk, dv, part, B, H, Hkv, T, D, window,
+                                scale, st);
+  if (Hkv != H) return hipErrorInvalidValue;  // the fp32 kernels take no K/V head groups
   return launch_bwd_dkdv_f32((const float *)q, (const float *)k, (const float *)v,
                              (const float *)dO, lse, delta, (float *)dk, (float *)dv, B, H, T, D,
                              window, scale, st);
@@ -65,9 +79,11 @@ hipError_t launch_bwd_dkdv(bool bf16, const void *q, const void *k, const void *
 
 hipError_t launch_bwd_dq(bool bf16, const void *q, const void *k, const void *v, const void *o,
                          const void *dO, const float *lse, float *delta, void *dq, int B, int H,
-                         int T, int D, int window, float scale, hipStream_t st) {
+                         int Hkv, int T, int D, int window, float scale, hipStream_t st) {
   if (bf16)
-    return launch_bwd_dq_bf16(q, k, v, o, dO, lse, delta, dq, B, H, T, D, window, scale, st);
+    return launch_bwd_dq_bf16(q, k, v, o, dO, lse, delta, dq, B, H, Hkv, T, D, window, scale,
+                              st);
+  if (Hkv != H) return hipErrorInvalidValue;  // the fp32 kernels take no K/V head groups
   // fp32: delta by its own kernel, then the dQ pass
   hipError_t e = launch_bwd_pre_f32((const float *)o, (const float *)dO, delta, B, H, T, D, st);
   if (e != hipSuccess) return e;
@@ -81,19 +97,22 @@ hipError_t launch_bwd_dq(bool bf16, const void *q, const void *k, const void *v,
 namespace {
 
 int bwd_all(bool bf16, const void *q, const void *k, const void *v, const void *o,
-            const void *dO, const float *lse, void *dq, void *dk, void *dv, int B, int H, int T,
-            int D, int window, float scale, void *workspace, hipStream_t st) {
+            const void *dO, const float *lse, void *dq, void *dk, void *dv, int B, int H,
+            int Hkv, int T, int D, int window, float scale, void *workspace, hipStream_t st) {
   int s = check_common(B, H, T, D, window);
+  if (s == SWATTN_OK) s = check_group(H, Hkv);
   if (s != SWATTN_OK) return s;
   if (!all_aligned({q, k, v, o, dO, dq, dk, dv, workspace}) || lse == nullptr)
     return SWATTN_ERR_INVALID_ARG;
-  // the dQ pass also writes delta, which the dK/dV pass then reads
+  // the dQ pass also writes delta, which the dK/dV pass then reads; with K/V head groups
+  // the per-query-head dK / dV partials follow it
   float *delta = (float *)workspace;
-  hipError_t e =
-      swattn::launch_bwd_dq(bf16, q, k, v, o, dO, lse, delta, dq, B, H, T, D, window, scale, st);
+  float *part = (float *)((char *)workspace + delta_bytes(B, H, T));
+  hipError_t e = swattn::launch_bwd_dq(bf16, q, k, v, o, dO, lse, delta, dq, B, H, Hkv, T, D,
+                                        window, scale, st);
   if (e == hipSuccess)
-    e = swattn::launch_bwd_dkdv(bf16, q, k, v, dO, lse, delta, dk, dv, B, H, T, D, window, scale,
-                                st);
+    e = swattn::launch_bwd_dkdv(bf16, q, k, v, dO, lse, delta, dk, dv, part, B, H, Hkv, T, D,
+                                window, scale, st);
   return hip_status(e);
 }
 
@@ -113,7 +132,7 @@ int bwd_dkdv(bool bf16, const void *q, const void *k, const void *v, const void 
   if (!all_aligned({q, k, v, dO, workspace, dk, dv}) || lse == nullptr)
     return SWATTN_ERR_INVALID_ARG;
   return hip_status(swattn::launch_bwd_dkdv(bf16, q, k, v, dO, lse, (const float *)workspace, dk,
-                                            dv, B, H, T, D, window, scale, st));
+                                            dv, nullptr, B, H, H, T, D, window, scale, st));
 }
 
 int bwd_dq(bool bf16, const void *q, const void *k, const void *v, const void *o,
@@ -124,7 +143,7 @@ int bwd_dq(bool bf16, const void *q, const void *k, const void *v, const void *o
   if (!all_aligned({q, k, v, o, dO, workspace, dq}) || lse == nullptr)
     return SWATTN_ERR_INVALID_ARG;
   return hip_status(swattn::launch_bwd_dq(bf16, q, k, v, o, dO, lse, (float *)workspace, dq, B,
-                                          H, T, D, window, scale, st));
+                                          H, H, T, D, window, scale, st));
 }
 
 }  // namespace
@@ -148,7 +167,18 @@ int swattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
   int st = check_common(B, H, T, D, window);
   if (st != SWATTN_OK) return st;
   if (!all_aligned({q, k, v, o}) || lse == nullptr) return SWATTN_ERR_INVALID_ARG;
-  return hip_status(swattn::launch_fwd_bf16(q, k, v, o, lse, B, H, T, D, window, scale,
+  return hip_status(swattn::launch_fwd_bf16(q, k, v, o, lse, B, H, H, T, D, window, scale,
+                                            (hipStream_t)stream));
+}
+
+int swattn_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                   int H, int Hkv, int T, int D, int window, float scale,
+                   swattn_stream_t stream) {
+  int st = check_common(B, H, T, D, window);
+  if (st == SWATTN_OK) st = check_group(H, Hkv);
+  if (st != SWATTN_OK) return st;
+  if (!all_aligned({q, k, v, o}) || lse == nullptr) return SWATTN_ERR_INVALID_ARG;
+  return hip_status(swattn::launch_fwd_bf16(q, k, v, o, lse, B, H, Hkv, T, D, window, scale,
                                             (hipStream_t)stream));
 }
 
@@ -163,23 +193,35 @@ int swattn_fwd_f32(const float *q, const float *k, const float *v, float *o, flo
 
 size_t swattn_bwd_workspace_size(int B, int H, int T, int D) {
   if (check_common(B, H, T, D, -1) != SWATTN_OK) return 0;
-  const size_t bytes = (size_t)B * H * T * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+  return delta_bytes(B, H, T);
+}
+
+size_t swattn_bwd_gqa_workspace_size(int B, int H, int Hkv, int T, int D) {
+  if (check_common(B, H, T, D, -1) != SWATTN_OK || check_group(H, Hkv) != SWATTN_OK) return 0;
+  if (Hkv == H) return delta_bytes(B, H, T);
+  return delta_bytes(B, H, T) + 2 * (size_t)B * T * H * D * sizeof(float);
 }
 
 int swattn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dO,
                const float *lse, void *dq, void *dk, void *dv, int B, int H, int T, int D,
                int window, float scale, void *workspace, swattn_stream_t stream) {
-  return bwd_all(true, q, k, v, o, dO, lse, dq, dk, dv, B, H, T, D, window, scale, workspace,
+  return bwd_all(true, q, k, v, o, dO, lse, dq, dk, dv, B, H, H, T, D, window, scale, workspace,
                  (hipStream_t)stream);
+}
+
+int swattn_bwd_gqa(const void *q, const void *k, const void *v, const void *o, const void *dO,
+                   const float *lse, void *dq, void *dk, void *dv, int B, int H, int Hkv, int T,
+                   int D, int window, float scale, void *workspace, swattn_stream_t stream) {
+  return bwd_all(true, q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, T, D, window, scale,
+                 workspace, (hipStream_t)stream);
 }
 
 int swattn_bwd_f32(const float *q, const float *k, const float *v, const float *o,
                    const float *dO, const float *lse, float *dq, float *dk, float *dv, int B,
                    int H, int T, int D, int window, float scale, void *workspace,
                    swattn_stream_t stream) {
-  return bwd_all(false, q, k, v, o, dO, lse, dq, dk, dv, B, H, T, D, window, scale, workspace,
-                 (hipStream_t)stream);
+  return bwd_all(false, q, k, v, o, dO, lse, dq, dk, dv, B, H, H, T, D, window, scale,
+                 workspace, (hipStream_t)stream);
 }
 
 int swattn_bwd_preprocess(const void *o, const void *dO, void *workspace, int B, int H, int T,
@@ -228,29 +270,38 @@ size_t swattn_decode_workspace_size(int B, int H, int D, int Tmax, int window) {
 }
 
 static int decode_common(bool bf16, const void *q, const void *k_cache, const void *v_cache,
-                         const int *seqlens, void *o, float *lse, int B, int H, int D, int Tmax,
-                         int window, float scale, void *workspace, swattn_stream_t stream) {
+                         const int *seqlens, void *o, float *lse, int B, int H, int Hkv, int D,
+                         int Tmax, int window, float scale, void *workspace,
+                         swattn_stream_t stream) {
   int st = check_decode(B, H, D, Tmax, window);
+  if (st == SWATTN_OK) st = check_group(H, Hkv);
   if (st != SWATTN_OK) return st;
   if (!all_aligned({q, k_cache, v_cache, o, workspace}) || seqlens == nullptr)
     return SWATTN_ERR_INVALID_ARG;
-  return hip_status(swattn::launch_decode(bf16, q, k_cache, v_cache, seqlens, o, lse, B, H, D,
-                                          Tmax, window, scale, (float *)workspace,
+  return hip_status(swattn::launch_decode(bf16, q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv,
+                                          D, Tmax, window, scale, (float *)workspace,
                                           (hipStream_t)stream));
 }
 
 int swattn_decode(const void *q, const void *k_cache, const void *v_cache, const int *seqlens,
                   void *o, float *lse, int B, int H, int D, int Tmax, int window, float scale,
                   void *workspace, swattn_stream_t stream) {
-  return decode_common(true, q, k_cache, v_cache, seqlens, o, lse, B, H, D, Tmax, window, scale,
-                       workspace, stream);
+  return decode_common(true, q, k_cache, v_cache, seqlens, o, lse, B, H, H, D, Tmax, window,
+                       scale, workspace, stream);
+}
+
+int swattn_decode_gqa(const void *q, const void *k_cache, const void *v_cache, const int *seqlens,
+                      void *o, float *lse, int B, int H, int Hkv, int D, int Tmax, int window,
+                      float scale, void *workspace, swattn_stream_t stream) {
+  return decode_common(true, q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, D, Tmax, window,
+                       scale, workspace, stream);
 }
 
 int swattn_decode_f32(const float *q, const float *k_cache, const float *v_cache,
                       const int *seqlens, float *o, float *lse, int B, int H, int D, int Tmax,
                       int window, float scale, void *workspace, swattn_stream_t stream) {
-  return decode_common(false, q, k_cache, v_cache, seqlens, o, lse, B, H, D, Tmax, window, scale,
-                       workspace, stream);
+  return decode_common(false, q, k_cache, v_cache, seqlens, o, lse, B, H, H, D, Tmax, window,
+                       scale, workspace, stream);
 }
 
 }  // extern "C"

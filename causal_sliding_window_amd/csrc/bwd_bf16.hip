@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ o,
     const uint16_t *__restrict__ dO, const float *__restrict__ lse, float *__restrict__ delta,
-    uint16_t *__restrict__ dq, int B, int H, int T, int window, float scale, int nqt) {
+    uint16_t *__restrict__ dq, int B, int H, int Hkv, int T, int window, float scale, int nqt) {
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::NSLOT * 2 * C::TSZ];  // [slot][K, V]
 
@@ -80,9 +80,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const int bh = bid % BH;
   const int b = bh / H, hh = bh % H;
   const int q0 = qt * C::BM;
-  const int rs = H * D;
+  const int rs = H * D;                // row stride of q, o, dO and dq
+  const int rsk = Hkv * D;             // row stride of k and v
+  const int hk = hh / (H / Hkv);       // the K/V head of query head hh
   const size_t base = ((size_t)b * T * H + hh) * D;
-  const uint16_t *qb = q + base, *kb = k + base, *vb = v + base, *gb = dO + base;
+  const size_t base_kv = ((size_t)b * T * Hkv + hk) * D;
+  const uint16_t *qb = q + base, *kb = k + base_kv, *vb = v + base_kv, *gb = dO + base;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in an SGPR
@@ -143,19 +146,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   // block db = (j % HALF) / RG, rows 16 ((j % HALF) % RG) .. + 15.
   const int rl = lane >> 2;
   const int lc = (lane & 3) ^ ((lane >> 4) & 3);  // logical chunk stored at this position
-  const uint32_t lane_off = (swap23(rl) * rs + 8 * lc) * 2;
-  // One buffer resource per tensor over all T rows of this (b, h): a tile's row
-  // offset goes into the lane offsets, and offsets from row T on read as zero.
+  const uint32_t lane_off = (swap23(rl) * rsk + 8 * lc) * 2;
+  // One buffer resource per tensor over all T rows of this (b, K/V head): a tile's
+  // row offset goes into the lane offsets, and offsets from row T on read as zero.
   const int my_tensor = (w * C::CPW) / C::HALF;  // every copy of a wave is K (0) or V (1)
-  const __amdgpu_buffer_rsrc_t rsrc_t = make_rsrc(my_tensor ? vb : kb, (uint32_t)T * rs * 2);
+  const __amdgpu_buffer_rsrc_t rsrc_t = make_rsrc(my_tensor ? vb : kb, (uint32_t)T * rsk * 2);
   auto issue_to = [&](int kt, uint16_t *tile) {
-    const uint32_t roff = (uint32_t)(kt * C::BN) * (uint32_t)rs * 2;
+    const uint32_t roff = (uint32_t)(kt * C::BN) * (uint32_t)rsk * 2;
 #pragma unroll
     for (int cc = 0; cc < C::CPW; ++cc) {
       const int jj = (w * C::CPW + cc) % C::HALF;
       const int db = jj / C::RG, row16 = 16 * (jj % C::RG);
       buf_copy16_to_lds(rsrc_t, tile + my_tensor * C::TSZ + db * (C::BN * 32) + row16 * 32,
-                        lane_off + (uint32_t)(row16 * rs + 32 * db) * 2 + roff);
+                        lane_off + (uint32_t)(row16 * rsk + 32 * db) * 2 + roff);
     }
   };
   auto k_tile = [&](int kt) { return smem + 2 * (kt & (C::NSLOT - 1)) * C::TSZ; };
@@ -357,17 +360,18 @@ hipError_t launch_bwd_pre_bf16(const void *o, const void *dO, float *delta, int 
 
 hipError_t launch_bwd_dq_bf16(const void *q, const void *k, const void *v, const void *o,
                               const void *dO, const float *lse, float *delta, void *dq, int B,
-                              int H, int T, int D, int window, float scale, hipStream_t st) {
+                              int H, int Hkv, int T, int D, int window, float scale,
+                              hipStream_t st) {
   const int nqt = (T + 127) / 128;
   const unsigned nb = (unsigned)(nqt * B * H);
   if (D == 128)
     bwd_dq_bf16_kernel<128><<<nb, 256, 0, st>>>(
         (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)o,
-        (const uint16_t *)dO, lse, delta, (uint16_t *)dq, B, H, T, window, scale, nqt);
+        (const uint16_t *)dO, lse, delta, (uint16_t *)dq, B, H, Hkv, T, window, scale, nqt);
   else
     bwd_dq_bf16_kernel<64><<<nb, 256, 0, st>>>(
         (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)o,
-        (const uint16_t *)dO, lse, delta, (uint16_t *)dq, B, H, T, window, scale, nqt);
+        (const uint16_t *)dO, lse, delta, (uint16_t *)dq, B, H, Hkv, T, window, scale, nqt);
   return hipGetLastError();
 }
 

@@ -2,10 +2,12 @@
 // engine decodes one token per step against the cache its attention kernels
 // read).  Bound by HBM: every visible K/V cache row is read exactly once.
 //
-// decode_split_kernel: workgroup (head h, chunk c, sequence b) reads seqlens[b] on
-//   the device, takes its kDecodeChunk rows of the visible range
-//   [max(0, L - W), L), and writes a partial (o_c normalised, lse_c) to the
-//   workspace (or o and lse directly when the visible range is one chunk).  Each
+// decode_split_kernel: workgroup (K/V head hk, chunk c, sequence b) reads seqlens[b]
+//   on the device, takes its kDecodeChunk rows of the visible range
+//   [max(0, L - W), L), and for each query head that reads K/V head hk (H / Hkv of
+//   them; one without grouping) writes a partial (o_c normalised, lse_c) to the
+//   workspace (or o and lse directly when the visible range is one chunk).  The
+//   cache rows are read once per group, not once per query head.  Each
 //   K/V row of one head is 256 contiguous bytes (bf16, D = 128) read by D/8 lanes
 //   with non-temporal 16-byte loads; every wave requests all of its rows before
 //   using any.
@@ -47,12 +49,15 @@ __device__ __forceinline__ int visible_lo(int L, int window) {
   return window > 0 ? max(0, L - window) : 0;
 }
 
-template <typename TT, int D>
+// GROUPED: more than one query head per K/V head (H > Hkv).  Without it the head loop
+// has one trip known at compile time, and the K/V rows need not stay in registers
+// after their use.
+template <typename TT, int D, bool GROUPED>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const TT *__restrict__ q, const TT *__restrict__ kc, const TT *__restrict__ vc,
     const int *__restrict__ seqlens, float *__restrict__ ws_o, float *__restrict__ ws_lse,
-    TT *__restrict__ o, float *__restrict__ lse, int H, int Tmax, int window, float scale,
-    int nsplit) {
+    TT *__restrict__ o, float *__restrict__ lse, int H, int Hkv, int Tmax, int window,
+    float scale, int nsplit) {
   constexpr int EPL = Elem<TT>::PER16;  // elements per 16-byte load
   constexpr int LPR = D / EPL;          // lanes per cache row
   constexpr int GPW = 64 / LPR;         // rows per wave and round
@@ -64,13 +69,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 
   // heads vary fastest across workgroups: the workgroups reading the rows of one
   // token range (adjacent 256-byte pieces of the same cache lines' DRAM pages) run together
-  const int hh = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
-  const int bh = b * H + hh;
+  const int hk = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+  const int G = GROUPED ? H / Hkv : 1;  // query heads hk * G .. hk * G + G - 1 read K/V head hk
   const int L = min(seqlens[b], Tmax);
   if (L <= 0) {  // empty sequence: o = 0, lse = -inf
     if (c == 0) {
-      for (int d = threadIdx.x; d < D; d += blockDim.x) o[(size_t)bh * D + d] = Elem<TT>::pack(0.f);
-      if (lse && threadIdx.x == 0) lse[bh] = -INFINITY;
+      for (int g = 0; g < G; ++g) {
+        const int bh = b * H + hk * G + g;
+        for (int d = threadIdx.x; d < D; d += blockDim.x)
+          o[(size_t)bh * D + d] = Elem<TT>::pack(0.f);
+        if (lse && threadIdx.x == 0) lse[bh] = -INFINITY;
+      }
     }
     return;
   }
@@ -82,9 +91,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int grp = lane / LPR, sl = lane % LPR;
-  const size_t rs = (size_t)H * D;
-  const TT *kb = kc + ((size_t)b * Tmax * H + hh) * D + sl * EPL;
-  const TT *vb = vc + ((size_t)b * Tmax * H + hh) * D + sl * EPL;
+  const size_t rs = (size_t)Hkv * D;
+  const TT *kb = kc + ((size_t)b * Tmax * Hkv + hk) * D + sl * EPL;
+  const TT *vb = vc + ((size_t)b * Tmax * Hkv + hk) * D + sl * EPL;
 
   // Every K and V row of this wave is requested before any is used.  Rows past the
   // chunk are read clamped to its last row and masked out below.
@@ -99,75 +108,85 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const int t = min(w * TPW + r * GPW + grp, cnt - 1);
     vr[r] = ldg16_stream(vb + (size_t)(t0 + t) * rs);
   }
-  float qf[EPL];
-  Elem<TT>::unpack(ldg16(q + ((size_t)b * H + hh) * D + sl * EPL), qf);
-
-  // scores of this wave's rows (each lane group holds one row per round)
-  float sc[ROUNDS];
-  float m = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < ROUNDS; ++r) {
-    float kf[EPL];
-    Elem<TT>::unpack(kr[r], kf);
-    float dot = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], kf[e], dot);
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, LPR);
-    const bool ok = w * TPW + r * GPW + grp < cnt;
-    sc[r] = ok ? dot * scale : -INFINITY;
-    m = fmaxf(m, sc[r]);
-  }
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-  const float mu = m == -INFINITY ? 0.f : m;
-  float lsum = 0.f, acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-#pragma unroll
-  for (int r = 0; r < ROUNDS; ++r) {
-    const float p = expf(sc[r] - mu);
-    lsum += p;
-    float vf[EPL];
-    Elem<TT>::unpack(vr[r], vf);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
-  }
-  // sum over the lane groups of the wave
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-    lsum += __shfl_xor(lsum, off);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], off);
-  }
-  if (grp == 0) {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) part_o[w][sl * EPL + e] = acc[e];
-    if (sl == 0) {
-      part_ml[w][0] = m;
-      part_ml[w][1] = lsum;
-    }
-  }
-  __syncthreads();
-  // merge the four wave partials (a wave without visible rows has m = -inf, l = 0)
-  const float M = fmaxf(fmaxf(part_ml[0][0], part_ml[1][0]), fmaxf(part_ml[2][0], part_ml[3][0]));
-  float f[4], Ltot = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[i] = part_ml[i][0] == -INFINITY ? 0.f : expf(part_ml[i][0] - M);
-    Ltot += f[i] * part_ml[i][1];
-  }
-  const size_t slot = (size_t)bh * nsplit + c;
+  // the query heads of the group in turn; each one's q row is requested one head ahead
+  const TT *qg = q + ((size_t)b * H + hk * G) * D + sl * EPL;
+  u32x4 qraw = ldg16(qg);
+  const size_t slot0 = ((size_t)b * H + hk * G) * nsplit + c;
   const int nch = (n + CH - 1) / CH;
-  if (tid < D) {
-    const float ov = (f[0] * part_o[0][tid] + f[1] * part_o[1][tid] + f[2] * part_o[2][tid] +
-                      f[3] * part_o[3][tid]) / Ltot;
-    if (nch == 1) o[(size_t)bh * D + tid] = Elem<TT>::pack(ov);  // nothing to merge
-    else ws_o[slot * D + tid] = ov;
-  }
-  if (tid == 0) {
-    if (nch > 1) ws_lse[slot] = M + logf(Ltot);
-    else if (lse) lse[bh] = M + logf(Ltot);
+  for (int g = 0; g < G; ++g) {
+    const int bh = b * H + hk * G + g;
+    const u32x4 qnext = g + 1 < G ? ldg16(qg + (size_t)(g + 1) * D) : qraw;
+    float qf[EPL];
+    Elem<TT>::unpack(qraw, qf);
+    qraw = qnext;
+
+    // scores of this wave's rows (each lane group holds one row per round)
+    float sc[ROUNDS];
+    float m = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      float kf[EPL];
+      Elem<TT>::unpack(kr[r], kf);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], kf[e], dot);
+#pragma unroll
+      for (int off = LPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, LPR);
+      const bool ok = w * TPW + r * GPW + grp < cnt;
+      sc[r] = ok ? dot * scale : -INFINITY;
+      m = fmaxf(m, sc[r]);
+    }
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    const float mu = m == -INFINITY ? 0.f : m;
+    float lsum = 0.f, acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const float p = expf(sc[r] - mu);
+      lsum += p;
+      float vf[EPL];
+      Elem<TT>::unpack(vr[r], vf);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+    }
+    // sum over the lane groups of the wave
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+      lsum += __shfl_xor(lsum, off);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], off);
+    }
+    if (grp == 0) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) part_o[w][sl * EPL + e] = acc[e];
+      if (sl == 0) {
+        part_ml[w][0] = m;
+        part_ml[w][1] = lsum;
+      }
+    }
+    __syncthreads();
+    // merge the four wave partials (a wave without visible rows has m = -inf, l = 0)
+    const float M = fmaxf(fmaxf(part_ml[0][0], part_ml[1][0]), fmaxf(part_ml[2][0], part_ml[3][0]));
+    float f[4], Ltot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = part_ml[i][0] == -INFINITY ? 0.f : expf(part_ml[i][0] - M);
+      Ltot += f[i] * part_ml[i][1];
+    }
+    const size_t slot = slot0 + (size_t)g * nsplit;
+    if (tid < D) {
+      const float ov = (f[0] * part_o[0][tid] + f[1] * part_o[1][tid] + f[2] * part_o[2][tid] +
+                        f[3] * part_o[3][tid]) / Ltot;
+      if (nch == 1) o[(size_t)bh * D + tid] = Elem<TT>::pack(ov);  // nothing to merge
+      else ws_o[slot * D + tid] = ov;
+    }
+    if (tid == 0) {
+      if (nch > 1) ws_lse[slot] = M + logf(Ltot);
+      else if (lse) lse[bh] = M + logf(Ltot);
+    }
+    __syncthreads();  // part_o / part_ml are written again for the next query head
   }
 }
 
@@ -256,13 +275,19 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 template <typename TT, int D>
 static hipError_t launch_decode_t(const void *q, const void *k_cache, const void *v_cache,
                                   const int *seqlens, void *o, float *lse, int B, int H,
-                                  int Tmax, int window, float scale, float *ws, hipStream_t st) {
+                                  int Hkv, int Tmax, int window, float scale, float *ws,
+                                  hipStream_t st) {
   const int ns = decode_num_splits(Tmax, window);
   float *ws_o = ws;
   float *ws_lse = ws + (size_t)B * H * ns * D;
-  decode_split_kernel<TT, D><<<dim3(H, ns, B), 256, 0, st>>>(
-      (const TT *)q, (const TT *)k_cache, (const TT *)v_cache, seqlens, ws_o, ws_lse, (TT *)o, lse,
-      H, Tmax, window, scale, ns);
+  if (Hkv != H)
+    decode_split_kernel<TT, D, true><<<dim3(Hkv, ns, B), 256, 0, st>>>(
+        (const TT *)q, (const TT *)k_cache, (const TT *)v_cache, seqlens, ws_o, ws_lse, (TT *)o,
+        lse, H, Hkv, Tmax, window, scale, ns);
+  else
+    decode_split_kernel<TT, D, false><<<dim3(Hkv, ns, B), 256, 0, st>>>(
+        (const TT *)q, (const TT *)k_cache, (const TT *)v_cache, seqlens, ws_o, ws_lse, (TT *)o,
+        lse, H, Hkv, Tmax, window, scale, ns);
   if (ns > 1)
     decode_merge_kernel<TT, D><<<B * H, 256, 0, st>>>(ws_o, ws_lse, seqlens, (TT *)o, lse, H, Tmax,
                                                       window, ns);
@@ -270,20 +295,20 @@ static hipError_t launch_decode_t(const void *q, const void *k_cache, const void
 }
 
 hipError_t launch_decode(bool bf16, const void *q, const void *k_cache, const void *v_cache,
-                         const int *seqlens, void *o, float *lse, int B, int H, int D, int Tmax,
-                         int window, float scale, float *ws, hipStream_t st) {
+                         const int *seqlens, void *o, float *lse, int B, int H, int Hkv, int D,
+                         int Tmax, int window, float scale, float *ws, hipStream_t st) {
   if (bf16) {
     if (D == 128)
-      return launch_decode_t<uint16_t, 128>(q, k_cache, v_cache, seqlens, o, lse, B, H, Tmax,
-                                            window, scale, ws, st);
-    return launch_decode_t<uint16_t, 64>(q, k_cache, v_cache, seqlens, o, lse, B, H, Tmax,
+      return launch_decode_t<uint16_t, 128>(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv,
+                                            Tmax, window, scale, ws, st);
+    return launch_decode_t<uint16_t, 64>(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, Tmax,
                                          window, scale, ws, st);
   }
   if (D == 128)
-    return launch_decode_t<float, 128>(q, k_cache, v_cache, seqlens, o, lse, B, H, Tmax, window,
-                                       scale, ws, st);
-  return launch_decode_t<float, 64>(q, k_cache, v_cache, seqlens, o, lse, B, H, Tmax, window,
-                                    scale, ws, st);
+    return launch_decode_t<float, 128>(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, Tmax,
+                                       window, scale, ws, st);
+  return launch_decode_t<float, 64>(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, Tmax,
+                                    window, scale, ws, st);
 }
 
 }  // namespace swattn

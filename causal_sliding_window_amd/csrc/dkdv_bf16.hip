@@ -42,12 +42,17 @@ struct DkdvCfg {
 // Largest P of a tile (any lane) from which P enters dV as bf16 hi + lo.
 constexpr float kLoP = 0.0625f;
 
-template <int D>
+// PARTIAL (grouped-query attention, H > Hkv): the workgroup's query head is one of
+// the G = H / Hkv that read K/V head h / G; it writes its fp32 contributions to dK
+// (already scaled) and dV to part_k / part_v, [B, T, H, D], and dkdv_group_sum_kernel
+// adds the G of each K/V head.  Otherwise dk and dv are written directly.
+template <int D, bool PARTIAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, uint16_t *__restrict__ dk,
-    uint16_t *__restrict__ dv, int B, int H, int T, int window, float scale, int nkt) {
+    uint16_t *__restrict__ dv, float *__restrict__ part_k, float *__restrict__ part_v, int B,
+    int H, int Hkv, int T, int window, float scale, int nkt) {
   using C = DkdvCfg<D>;
   // One LDS array (with a single __shared__ variable the compiler keeps the restrict
   // scopes below): [slot][Q, dO][TSZ] bf16, then [slot][lse, delta, spare, spare][64]
@@ -62,9 +67,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   const int bh = bid % BH;
   const int b = bh / H, hh = bh % H;
   const int k0 = kt * C::BK;
-  const int rs = H * D;
+  const int rs = H * D;       // row stride of q and dO (and of the partials)
+  const int rsk = Hkv * D;    // row stride of k, v, dk and dv
+  const int hk = hh / (H / Hkv);  // the K/V head of query head hh
   const size_t base = ((size_t)b * T * H + hh) * D;
-  const uint16_t *qb = q + base, *kb = k + base, *vb = v + base, *gb = dO + base;
+  const size_t base_kv = ((size_t)b * T * Hkv + hk) * D;
+  const uint16_t *qb = q + base, *kb = k + base_kv, *vb = v + base_kv, *gb = dO + base;
   const float *lseb = lse + (size_t)bh * T, *delb = delta + (size_t)bh * T;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -366,11 +374,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // tiles (vector-memory operations complete in order).
   for (int t = qt0; t < qt0 + 4; ++t) issue(t);
   {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)T * rs * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)T * rs * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)T * rsk * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)T * rsk * 2);
 #pragma unroll
     for (int st = 0; st < C::KST; ++st) {
-      const uint32_t off = (my_k * rs + 16 * st + 8 * h) * 2;
+      const uint32_t off = (my_k * rsk + 16 * st + 8 * h) * 2;
       kr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
       vr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
@@ -465,8 +473,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm<0>);  // no copy into LDS outlives the workgroup
 
-  if (my_k < T) {
-    uint16_t *dkb = dk + base + (size_t)my_k * rs, *dvb = dv + base + (size_t)my_k * rs;
+  if (PARTIAL) {
+    if (my_k < T) {
+      float *pk = part_k + base + (size_t)my_k * rs, *pv = part_v + base + (size_t)my_k * rs;
+#pragma unroll
+      for (int d = 0; d < C::NDB; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 a, c4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] = dka[d][4 * g + e] * scale;
+            c4[e] = dva[d][4 * g + e];
+          }
+          *reinterpret_cast<f32x4 *>(pk + 32 * d + 8 * g + 4 * h) = a;
+          *reinterpret_cast<f32x4 *>(pv + 32 * d + 8 * g + 4 * h) = c4;
+        }
+    }
+  } else if (my_k < T) {
+    uint16_t *dkb = dk + base_kv + (size_t)my_k * rsk, *dvb = dv + base_kv + (size_t)my_k * rsk;
 #pragma unroll
     for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
@@ -483,19 +508,83 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   }
 }
 
-hipError_t launch_bwd_dkdv_bf16(const void *q, const void *k, const void *v, const void *dO,
-                                const float *lse, const float *delta, void *dk, void *dv, int B,
-                                int H, int T, int D, int window, float scale, hipStream_t st) {
-  const int nkt = (T + DkdvCfg<128>::BK - 1) / DkdvCfg<128>::BK;
+// dk, dv [B, T, Hkv, D] (bf16) = sums of the G = H / Hkv partials [B, T, H, D] (fp32)
+// of each K/V head, in head order; 8 elements per thread.
+__global__ __launch_bounds__(256) void dkdv_group_sum_kernel(const float *__restrict__ part_k,
+                                                             const float *__restrict__ part_v,
+                                                             uint16_t *__restrict__ dk,
+                                                             uint16_t *__restrict__ dv,
+                                                             long long n8, int G, int D) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // group of 8 outputs
+  if (i >= n8) return;
+  const long long e = i * 8;               // output element: ((b T + t) Hkv + hk) D + d
+  const long long row = e / D, d = e % D;  // row = (b T + t) Hkv + hk
+  const float *pk = part_k + row * G * D + d, *pv = part_v + row * G * D + d;
+  float sk[8], sv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sk[j] = sv[j] = 0.f;
+  for (int g = 0; g < G; ++g) {
+    const f32x4 k0 = *reinterpret_cast<const f32x4 *>(pk + (size_t)g * D);
+    const f32x4 k1 = *reinterpret_cast<const f32x4 *>(pk + (size_t)g * D + 4);
+    const f32x4 v0 = *reinterpret_cast<const f32x4 *>(pv + (size_t)g * D);
+    const f32x4 v1 = *reinterpret_cast<const f32x4 *>(pv + (size_t)g * D + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sk[j] += k0[j];
+      sk[4 + j] += k1[j];
+      sv[j] += v0[j];
+      sv[4 + j] += v1[j];
+    }
+  }
+  bf16x4 a0, a1, b0, b1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a0[j] = (__bf16)sk[j];
+    a1[j] = (__bf16)sk[4 + j];
+    b0[j] = (__bf16)sv[j];
+    b1[j] = (__bf16)sv[4 + j];
+  }
+  *reinterpret_cast<bf16x4 *>(dk + e) = a0;
+  *reinterpret_cast<bf16x4 *>(dk + e + 4) = a1;
+  *reinterpret_cast<bf16x4 *>(dv + e) = b0;
+  *reinterpret_cast<bf16x4 *>(dv + e + 4) = b1;
+}
+
+template <int D, bool PARTIAL>
+static void launch_dkdv_t(const void *q, const void *k, const void *v, const void *dO,
+                          const float *lse, const float *delta, void *dk, void *dv,
+                          float *part_k, float *part_v, int B, int H, int Hkv, int T, int window,
+                          float scale, hipStream_t st) {
+  const int nkt = (T + DkdvCfg<D>::BK - 1) / DkdvCfg<D>::BK;
   const unsigned nb = (unsigned)(nkt * B * H);
+  bwd_dkdv_bf16_kernel<D, PARTIAL><<<nb, 256, 0, st>>>(
+      (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dO, lse,
+      delta, (uint16_t *)dk, (uint16_t *)dv, part_k, part_v, B, H, Hkv, T, window, scale, nkt);
+}
+
+hipError_t launch_bwd_dkdv_bf16(const void *q, const void *k, const void *v, const void *dO,
+                                const float *lse, const float *delta, void *dk, void *dv,
+                                float *part, int B, int H, int Hkv, int T, int D, int window,
+                                float scale, hipStream_t st) {
+  if (Hkv == H) {
+    if (D == 128)
+      launch_dkdv_t<128, false>(q, k, v, dO, lse, delta, dk, dv, nullptr, nullptr, B, H, Hkv, T,
+                                window, scale, st);
+    else
+      launch_dkdv_t<64, false>(q, k, v, dO, lse, delta, dk, dv, nullptr, nullptr, B, H, Hkv, T,
+                               window, scale, st);
+    return hipGetLastError();
+  }
+  float *part_k = part, *part_v = part + (size_t)B * T * H * D;
   if (D == 128)
-    bwd_dkdv_bf16_kernel<128><<<nb, 256, 0, st>>>(
-        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dO, lse,
-        delta, (uint16_t *)dk, (uint16_t *)dv, B, H, T, window, scale, nkt);
+    launch_dkdv_t<128, true>(q, k, v, dO, lse, delta, dk, dv, part_k, part_v, B, H, Hkv, T,
+                             window, scale, st);
   else
-    bwd_dkdv_bf16_kernel<64><<<nb, 256, 0, st>>>(
-        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dO, lse,
-        delta, (uint16_t *)dk, (uint16_t *)dv, B, H, T, window, scale, nkt);
+    launch_dkdv_t<64, true>(q, k, v, dO, lse, delta, dk, dv, part_k, part_v, B, H, Hkv, T,
+                            window, scale, st);
+  const long long n8 = (long long)B * T * Hkv * D / 8;
+  dkdv_group_sum_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(
+      part_k, part_v, (uint16_t *)dk, (uint16_t *)dv, n8, H / Hkv, D);
   return hipGetLastError();
 }
 

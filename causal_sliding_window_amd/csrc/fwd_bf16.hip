@@ -46,7 +46,7 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
-    int B, int H, int T, int window, float scale, int nqt) {
+    int B, int H, int Hkv, int T, int window, float scale, int nqt) {
   using C = FwdCfg<D>;
   // [slot][K, V][TSZ]
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * C::TSZ];
@@ -57,9 +57,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int bh = bid % BH;            // consecutive blocks: different heads
   const int b = bh / H, hh = bh % H;
   const int q0 = qt * C::BM;
-  const int rs = H * D;                // row stride (elements)
+  const int rs = H * D;                // row stride of q and o (elements)
+  const int rsk = Hkv * D;             // row stride of k and v
+  const int hk = hh / (H / Hkv);       // the K/V head of query head hh
   const size_t base = ((size_t)b * T * H + hh) * D;
-  const uint16_t *qb = q + base, *kb = k + base, *vb = v + base;
+  const size_t base_kv = ((size_t)b * T * Hkv + hk) * D;
+  const uint16_t *qb = q + base, *kb = k + base_kv, *vb = v + base_kv;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in an SGPR
@@ -94,20 +97,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   // Lane part of the source offset; this wave issues copies CPW w .. CPW w + CPW - 1.
   const int rl = lane >> 2;                          // LDS row within the 16-row group
   const int lc = (lane & 3) ^ ((lane >> 4) & 3);     // logical chunk stored at this position
-  const uint32_t klane = (swap23(rl) * rs + 8 * lc) * 2;
-  const uint32_t vlane = (rl * rs + 8 * lc) * 2;
+  const uint32_t klane = (swap23(rl) * rsk + 8 * lc) * 2;
+  const uint32_t vlane = (rl * rsk + 8 * lc) * 2;
   auto issue = [&](int tensor, int kt, int slot) {
     const uint16_t *src = tensor ? vb : kb;
     const int row0 = kt * C::BN;
     const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(src + (size_t)row0 * rs, (uint32_t)(T - row0) * rs * 2);
+        make_rsrc(src + (size_t)row0 * rsk, (uint32_t)(T - row0) * rsk * 2);
     uint16_t *tile = smem + (2 * slot + tensor) * C::TSZ;
 #pragma unroll
     for (int cc = 0; cc < C::CPW; ++cc) {
       const int j = C::CPW * w + cc;
       const int db = j / C::RG, row16 = 16 * (j % C::RG);
       buf_copy16_to_lds(r, tile + db * (C::BN * 32) + row16 * 32,
-                        (tensor ? vlane : klane) + (row16 * rs + 32 * db) * 2);
+                        (tensor ? vlane : klane) + (row16 * rsk + 32 * db) * 2);
     }
   };
 
@@ -362,17 +365,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 }
 
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
-                           int B, int H, int T, int D, int window, float scale, hipStream_t st) {
+                           int B, int H, int Hkv, int T, int D, int window, float scale,
+                           hipStream_t st) {
   const int nqt = (T + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
   dim3 grid((unsigned)(nqt * B * H)), block(256);
   if (D == 128)
     fwd_bf16_kernel<128><<<grid, block, 0, st>>>((const uint16_t *)q, (const uint16_t *)k,
                                                  (const uint16_t *)v, (uint16_t *)o, lse, B, H,
-                                                 T, window, scale, nqt);
+                                                 Hkv, T, window, scale, nqt);
   else
     fwd_bf16_kernel<64><<<grid, block, 0, st>>>((const uint16_t *)q, (const uint16_t *)k,
-                                                (const uint16_t *)v, (uint16_t *)o, lse, B, H, T,
-                                                window, scale, nqt);
+                                                (const uint16_t *)v, (uint16_t *)o, lse, B, H,
+                                                Hkv, T, window, scale, nqt);
   return hipGetLastError();
 }
 

@@ -11,31 +11,37 @@ constexpr int kDecodeChunk = 128;
 
 int decode_num_splits(int Tmax, int window);
 
+// Hkv: K/V heads (H, or a divisor of H: query head h reads K/V head h / (H / Hkv)).
+// The fp32 kernels take no Hkv (they serve H == Hkv only).
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
-                           int B, int H, int T, int D, int window, float scale, hipStream_t st);
+                           int B, int H, int Hkv, int T, int D, int window, float scale,
+                           hipStream_t st);
 hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                           int B, int H, int T, int D, int window, float scale, hipStream_t st);
 
 // Backward passes; `bf16` selects the bf16 MFMA kernels, else the fp32 ones.
 hipError_t launch_bwd_pre(bool bf16, const void *o, const void *dO, float *delta, int B, int H,
                           int T, int D, hipStream_t st);
+// With Hkv < H, `part` holds 2 * B*T*H*D floats: per-query-head partials of dK, dV.
 hipError_t launch_bwd_dkdv(bool bf16, const void *q, const void *k, const void *v,
                            const void *dO, const float *lse, const float *delta, void *dk,
-                           void *dv, int B, int H, int T, int D, int window, float scale,
-                           hipStream_t st);
+                           void *dv, float *part, int B, int H, int Hkv, int T, int D,
+                           int window, float scale, hipStream_t st);
 // dQ pass; also computes delta = rowsum(dO * o) and writes it to `delta`.
 hipError_t launch_bwd_dq(bool bf16, const void *q, const void *k, const void *v, const void *o,
                          const void *dO, const float *lse, float *delta, void *dq, int B, int H,
-                         int T, int D, int window, float scale, hipStream_t st);
+                         int Hkv, int T, int D, int window, float scale, hipStream_t st);
 
 hipError_t launch_bwd_pre_bf16(const void *o, const void *dO, float *delta, int B, int H, int T,
                                int D, hipStream_t st);
 hipError_t launch_bwd_dkdv_bf16(const void *q, const void *k, const void *v, const void *dO,
-                                const float *lse, const float *delta, void *dk, void *dv, int B,
-                                int H, int T, int D, int window, float scale, hipStream_t st);
+                                const float *lse, const float *delta, void *dk, void *dv,
+                                float *part, int B, int H, int Hkv, int T, int D, int window,
+                                float scale, hipStream_t st);
 hipError_t launch_bwd_dq_bf16(const void *q, const void *k, const void *v, const void *o,
                               const void *dO, const float *lse, float *delta, void *dq, int B,
-                              int H, int T, int D, int window, float scale, hipStream_t st);
+                              int H, int Hkv, int T, int D, int window, float scale,
+                              hipStream_t st);
 hipError_t launch_bwd_pre_f32(const float *o, const float *dO, float *delta, int B, int H, int T,
                               int D, hipStream_t st);
 hipError_t launch_bwd_dkdv_f32(const float *q, const float *k, const float *v, const float *dO,
@@ -46,7 +52,7 @@ hipError_t launch_bwd_dq_f32(const float *q, const float *k, const float *v, con
                              int D, int window, float scale, hipStream_t st);
 
 hipError_t launch_decode(bool bf16, const void *q, const void *k_cache, const void *v_cache,
-                         const int *seqlens, void *o, float *lse, int B, int H, int D, int Tmax,
-                         int window, float scale, float *ws, hipStream_t st);
+                         const int *seqlens, void *o, float *lse, int B, int H, int Hkv, int D,
+                         int Tmax, int window, float scale, float *ws, hipStream_t st);
 
 }  // namespace swattn

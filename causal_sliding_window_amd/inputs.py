@@ -57,12 +57,14 @@ def _rms_normalize(x: torch.Tensor) -> torch.Tensor:
 
 
 def training_inputs(B: int, T: int, H: int, D: int, dtype: str = "bf16",
-                    seed: int = 0, qk_norm: bool = False) -> dict:
-    """q, k, v, dO as CPU tensors [B, T, H, D] in ``dtype`` ("bf16" or "f32")."""
+                    seed: int = 0, qk_norm: bool = False, Hkv: int | None = None) -> dict:
+    """q, dO as CPU tensors [B, T, H, D] and k, v [B, T, Hkv, D] (Hkv = H by default) in
+    ``dtype`` ("bf16" or "f32")."""
     shape = (B, T, H, D)
+    kv_shape = (B, T, H if Hkv is None else Hkv, D)
     q = _randn(shape, seed)
-    k = _randn(shape, seed + 1)
-    v = _randn(shape, seed + 2)
+    k = _randn(kv_shape, seed + 1)
+    v = _randn(kv_shape, seed + 2)
     do = _randn(shape, seed + 3)
     if qk_norm:
         q = _rms_normalize(q)
@@ -78,15 +80,17 @@ def decode_lengths(B: int, seed: int = 7, lo: int = 512, hi: int = 4096) -> np.n
 
 
 def decode_inputs(B: int, H: int, D: int, Tmax: int, dtype: str = "bf16",
-                  seed: int = 7, lengths=None) -> dict:
-    """q [B, H, D], k/v caches [B, Tmax, H, D] and int32 seqlens [B] (CPU)."""
+                  seed: int = 7, lengths=None, Hkv: int | None = None) -> dict:
+    """q [B, H, D], k/v caches [B, Tmax, Hkv, D] (Hkv = H by default) and int32
+    seqlens [B] (CPU)."""
     td = DTYPES[dtype]
     if lengths is None:
         lengths = decode_lengths(B, seed=7, lo=min(512, Tmax), hi=Tmax)
     seqlens = torch.as_tensor(np.asarray(lengths, dtype=np.int32))
     q = _randn((B, H, D), seed).to(td)
-    k = _randn((B, Tmax, H, D), seed + 1).to(td)
-    v = _randn((B, Tmax, H, D), seed + 2).to(td)
+    Hkv = H if Hkv is None else Hkv
+    k = _randn((B, Tmax, Hkv, D), seed + 1).to(td)
+    v = _randn((B, Tmax, Hkv, D), seed + 2).to(td)
     return {"q": q, "k_cache": k, "v_cache": v, "seqlens": seqlens}
 
 

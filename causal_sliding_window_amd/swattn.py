@@ -6,7 +6,8 @@ that live on the GPU; every step of the computation runs in the HIP kernels of
 fallback: if the library is missing or fails to load, every call raises.
 
 Convenience wrappers ``fwd``, ``bwd`` and ``decode`` allocate the outputs (and the
-workspace) with torch and call the matching entry point for the input dtype.
+workspace) with torch and call the matching entry point for the input dtype; with
+fewer K/V heads than query heads they call the grouped-query (``*_gqa``) entries.
 """
 
 from __future__ import annotations
@@ -44,6 +45,10 @@ _SIGS = {
     "swattn_decode_workspace_size": ([_I] * 5, ctypes.c_size_t),
     "swattn_decode": ([_P] * 6 + [_I] * 5 + [_F, _P, _P], _I),
     "swattn_decode_f32": ([_P] * 6 + [_I] * 5 + [_F, _P, _P], _I),
+    "swattn_fwd_gqa": ([_P] * 5 + [_I] * 6 + [_F, _P], _I),
+    "swattn_bwd_gqa_workspace_size": ([_I] * 5, ctypes.c_size_t),
+    "swattn_bwd_gqa": ([_P] * 9 + [_I] * 6 + [_F, _P, _P], _I),
+    "swattn_decode_gqa": ([_P] * 6 + [_I] * 6 + [_F, _P, _P], _I),
 }
 
 
@@ -220,6 +225,71 @@ def swattn_decode(q, k_cache, v_cache, seqlens, o, lse, window: int, scale: floa
 swattn_decode_f32 = swattn_decode
 
 
+# ----------------------------------------------------------------------------- grouped-query entries
+def _groups(H, Hkv):
+    if Hkv <= 0 or H % Hkv:
+        raise SwattnError(f"{H} query heads cannot share {Hkv} K/V heads in equal groups")
+
+
+def swattn_fwd_gqa(q, k, v, o, lse, window: int, scale: float, stream=None):
+    """Grouped-query forward (bf16): q, o [B,T,H,D]; k, v [B,T,Hkv,D]; lse [B,H,T]."""
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    _groups(H, Hkv)
+    for n, t, h in (("q", q, H), ("k", k, Hkv), ("v", v, Hkv), ("o", o, H)):
+        _dev_tensor(t, n, torch.bfloat16, (B, T, h, D))
+    _dev_tensor(lse, "lse", torch.float32, (B, H, T))
+    _check(lib().swattn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, T, D,
+                                int(window), float(scale), _stream(stream, q.device)),
+           "swattn_fwd_gqa")
+
+
+def swattn_bwd_gqa_workspace_size(B: int, H: int, Hkv: int, T: int, D: int) -> int:
+    return int(lib().swattn_bwd_gqa_workspace_size(B, H, Hkv, T, D))
+
+
+def swattn_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, window: int, scale: float, workspace,
+                   stream=None):
+    """Grouped-query backward (bf16): dq [B,T,H,D]; dk, dv [B,T,Hkv,D] (sums over each
+    K/V head's query heads)."""
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    _groups(H, Hkv)
+    for n, t, h in (("q", q, H), ("k", k, Hkv), ("v", v, Hkv), ("o", o, H), ("do", do, H),
+                    ("dq", dq, H), ("dk", dk, Hkv), ("dv", dv, Hkv)):
+        _dev_tensor(t, n, torch.bfloat16, (B, T, h, D))
+    _dev_tensor(lse, "lse", torch.float32, (B, H, T))
+    _dev_tensor(workspace, "workspace")
+    if workspace.numel() * workspace.element_size() < swattn_bwd_gqa_workspace_size(B, H, Hkv, T,
+                                                                                     D):
+        raise SwattnError("workspace too small")
+    _check(lib().swattn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                                _ptr(dk), _ptr(dv), B, H, Hkv, T, D, int(window), float(scale),
+                                _ptr(workspace), _stream(stream, q.device)), "swattn_bwd_gqa")
+
+
+def swattn_decode_gqa(q, k_cache, v_cache, seqlens, o, lse, window: int, scale: float,
+                      workspace, stream=None):
+    """Grouped-query decode (bf16): q, o [B,H,D]; k_cache, v_cache [B,Tmax,Hkv,D]."""
+    B, H, D = q.shape
+    Tmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _groups(H, Hkv)
+    _dev_tensor(q, "q", torch.bfloat16, (B, H, D))
+    _dev_tensor(o, "o", torch.bfloat16, (B, H, D))
+    _dev_tensor(k_cache, "k_cache", torch.bfloat16, (B, Tmax, Hkv, D))
+    _dev_tensor(v_cache, "v_cache", torch.bfloat16, (B, Tmax, Hkv, D))
+    _dev_tensor(seqlens, "seqlens", torch.int32, (B,))
+    if lse is not None:
+        _dev_tensor(lse, "lse", torch.float32, (B, H))
+    _dev_tensor(workspace, "workspace")
+    if workspace.numel() * workspace.element_size() < swattn_decode_workspace_size(B, H, D, Tmax, window):
+        raise SwattnError("workspace too small")
+    _check(lib().swattn_decode_gqa(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o),
+                                   _ptr(lse), B, H, Hkv, D, Tmax, int(window), float(scale),
+                                   _ptr(workspace), _stream(stream, q.device)),
+           "swattn_decode_gqa")
+
+
 # ----------------------------------------------------------------------------- allocating wrappers
 def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
@@ -230,7 +300,10 @@ def fwd(q, k, v, window: int = -1, scale: float | None = None, stream=None):
     scale = default_scale(D) if scale is None else scale
     o = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    swattn_fwd(q, k, v, o, lse, window, scale, stream)
+    if k.shape[2] != H:
+        swattn_fwd_gqa(q, k, v, o, lse, window, scale, stream)
+    else:
+        swattn_fwd(q, k, v, o, lse, window, scale, stream)
     return o, lse
 
 
@@ -239,10 +312,14 @@ def bwd(q, k, v, o, do, lse, window: int = -1, scale: float | None = None, strea
     B, T, H, D = q.shape
     scale = default_scale(D) if scale is None else scale
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    Hkv = k.shape[2]
     if workspace is None:
-        workspace = torch.empty(swattn_bwd_workspace_size(B, H, T, D), dtype=torch.uint8,
+        workspace = torch.empty(swattn_bwd_gqa_workspace_size(B, H, Hkv, T, D), dtype=torch.uint8,
                                 device=q.device)
-    swattn_bwd(q, k, v, o, do, lse, dq, dk, dv, window, scale, workspace, stream)
+    if Hkv != H:
+        swattn_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, window, scale, workspace, stream)
+    else:
+        swattn_bwd(q, k, v, o, do, lse, dq, dk, dv, window, scale, workspace, stream)
     return dq, dk, dv
 
 
@@ -256,5 +333,8 @@ def decode(q, k_cache, v_cache, seqlens, window: int = -1, scale: float | None =
     if workspace is None:
         workspace = torch.empty(swattn_decode_workspace_size(B, H, D, Tmax, window),
                                 dtype=torch.uint8, device=q.device)
-    swattn_decode(q, k_cache, v_cache, seqlens, o, lse, window, scale, workspace, stream)
+    if k_cache.shape[2] != H:
+        swattn_decode_gqa(q, k_cache, v_cache, seqlens, o, lse, window, scale, workspace, stream)
+    else:
+        swattn_decode(q, k_cache, v_cache, seqlens, o, lse, window, scale, workspace, stream)
     return o, lse

@@ -13,6 +13,9 @@
  *     kernels are faster and take the window_size argument.
  *   - same guide, section 6 "Inference engine": the engine keeps a KV cache that
  *     the kernels read (with-KV-cache entry) while decoding one token at a time.
+ *   - same guide, section 1 feature list: grouped-query attention, fewer K/V heads
+ *     than query heads (the *_gqa entry points; the one-K/V-head case is the
+ *     multi-query attention of the release article's architecture list).
  *
  * Definitions used by every entry point (positions are 0-based):
  *   visible(i, j)  <=>  j <= i  and  (window < 0  or  i - j < window)
@@ -27,6 +30,10 @@
  *     Plain names take bf16 (raw 16-bit storage); the _f32 names take float32.
  *   - lse: device float32 [B, H, T].  Decode q/o: [B, H, D]; decode lse: [B, H].
  *   - k_cache, v_cache: device, contiguous [B, Tmax, H, D].
+ *   - *_gqa entry points: k, v, dk, dv are [B, T, Hkv, D] and k_cache, v_cache
+ *     [B, Tmax, Hkv, D], with Hkv >= 1 dividing H.  Query head h reads K/V head
+ *     h / (H / Hkv) (contiguous groups; the pages do not say which heads share,
+ *     this is the plain reading), and dk, dv of a K/V head sum over its group.
  *   - seqlens: device int32 [B].
  *   - D must be 64 or 128.  All arithmetic accumulates in float32; bf16 outputs
  *     are rounded to nearest even.
@@ -42,6 +49,7 @@
  *
  * Errors: every entry point returns a swattn_status; nothing is thrown.
  *   SWATTN_ERR_INVALID_ARG  NULL required pointer, B/H/T/D/Tmax <= 0, window == 0,
+ *                           Hkv <= 0 or not dividing H (*_gqa),
  *                           a size product that does not fit the kernels' 32-bit
  *                           grid/row indices, or a workspace pointer of NULL
  *   SWATTN_ERR_UNSUPPORTED  D not in {64, 128}, or (for the training calls) one
@@ -86,6 +94,11 @@ int swattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 int swattn_fwd_f32(const float *q, const float *k, const float *v, float *o,
                    float *lse, int B, int H, int T, int D, int window,
                    float scale, swattn_stream_t stream);
+/* Grouped-query forward (bf16): k, v [B,T,Hkv,D]; otherwise as swattn_fwd, which it
+ * equals for Hkv == H. */
+int swattn_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int B, int H, int Hkv, int T, int D, int window, float scale,
+                   swattn_stream_t stream);
 
 /*
  * Backward workspace in bytes: delta_i = dO_i . o_i, float32 [B,H,T], rounded up
@@ -109,6 +122,19 @@ int swattn_bwd_f32(const float *q, const float *k, const float *v,
                    const float *o, const float *dO, const float *lse, float *dq,
                    float *dk, float *dv, int B, int H, int T, int D, int window,
                    float scale, void *workspace, swattn_stream_t stream);
+/* Grouped-query backward workspace in bytes: delta (as swattn_bwd_workspace_size)
+ * and, when Hkv < H, float32 partials of dk and dv per query head, 2*B*T*H*D*4
+ * bytes.  Returns 0 for invalid sizes. */
+size_t swattn_bwd_gqa_workspace_size(int B, int H, int Hkv, int T, int D);
+/* Grouped-query backward (bf16): k, v, dk, dv [B,T,Hkv,D]; dk and dv of a K/V head
+ * sum the gradients of its H / Hkv query heads.  The dK/dV pass writes each query
+ * head's float32 contribution to the workspace and a second kernel adds the heads
+ * of each group in head order: no atomics, bitwise reproducible.  `workspace` must
+ * hold swattn_bwd_gqa_workspace_size() bytes; equals swattn_bwd for Hkv == H. */
+int swattn_bwd_gqa(const void *q, const void *k, const void *v, const void *o,
+                   const void *dO, const float *lse, void *dq, void *dk, void *dv,
+                   int B, int H, int Hkv, int T, int D, int window, float scale,
+                   void *workspace, swattn_stream_t stream);
 
 /*
  * The passes of swattn_bwd, callable on their own (to time them, or to overlap
@@ -165,6 +191,14 @@ int swattn_decode_f32(const float *q, const float *k_cache,
                       const float *v_cache, const int *seqlens, float *o,
                       float *lse, int B, int H, int D, int Tmax, int window,
                       float scale, void *workspace, swattn_stream_t stream);
+/* Grouped-query decode (bf16): k_cache, v_cache [B,Tmax,Hkv,D]; each cache row is
+ * read once for the H / Hkv query heads of its group.  The workspace is
+ * swattn_decode_workspace_size(B, H, D, Tmax, window) bytes (partials per query
+ * head); otherwise as swattn_decode. */
+int swattn_decode_gqa(const void *q, const void *k_cache, const void *v_cache,
+                      const int *seqlens, void *o, float *lse, int B, int H, int Hkv,
+                      int D, int Tmax, int window, float scale, void *workspace,
+                      swattn_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -95,6 +95,33 @@ def test_bwd_and_decode_argument_errors():
     assert lib.swattn_decode_f32(*p6n, 1, 1, 128, 16, -1, 1.0, FAKE, None) == 1
 
 
+def test_gqa_entry_points_declared_and_sized():
+    names = declared_functions()
+    for n in ("swattn_fwd_gqa", "swattn_bwd_gqa", "swattn_bwd_gqa_workspace_size",
+              "swattn_decode_gqa"):
+        assert n in names
+    ws = swattn.swattn_bwd_gqa_workspace_size
+    assert ws(8, 6, 6, 2048, 128) == swattn.swattn_bwd_workspace_size(8, 6, 2048, 128)
+    # delta plus float32 dK and dV partials per query head
+    assert ws(8, 6, 2, 2048, 128) == 8 * 6 * 2048 * 4 + 2 * 8 * 2048 * 6 * 128 * 4
+    assert ws(8, 6, 4, 2048, 128) == 0       # 6 heads do not split into 4 groups
+    assert ws(8, 6, 0, 2048, 128) == 0
+
+
+def test_gqa_argument_errors():
+    lib = swattn.lib()
+    # q, k, v, o, lse, B, H, Hkv, T, D, window, scale, stream
+    assert lib.swattn_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 6, 4, 8, 64, -1, 1.0, None) == 1
+    assert lib.swattn_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 6, 0, 8, 64, -1, 1.0, None) == 1
+    assert lib.swattn_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 6, 3, 8, 96, -1, 1.0, None) == 2
+    p9 = [FAKE] * 9
+    assert lib.swattn_bwd_gqa(*p9, 1, 6, 5, 8, 64, -1, 1.0, FAKE, None) == 1
+    assert lib.swattn_bwd_gqa(*p9, 1, 6, 3, 8, 64, 0, 1.0, FAKE, None) == 1
+    p6 = [FAKE] * 6
+    assert lib.swattn_decode_gqa(*p6, 1, 6, 4, 128, 16, -1, 1.0, FAKE, None) == 1
+    assert lib.swattn_decode_gqa(*p6, 1, 6, 2, 80, 16, -1, 1.0, FAKE, None) == 2
+
+
 def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(swattn.SwattnError):
