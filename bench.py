@@ -90,10 +90,13 @@ def step_accounting(B, H, T, D, windows):
     return out
 
 
-def decode_bytes(lengths, H, D, W, elem=2):
+def decode_bytes(lengths, H, D, W, elem=2, Hkv=None):
+    """Visible K and V rows of the Hkv cache heads read once, q and o of the H query heads,
+    and lse."""
+    Hkv = H if Hkv is None else Hkv
     vis = sum(min(int(L), W) if W > 0 else int(L) for L in lengths)
     B = len(lengths)
-    return 2 * vis * H * D * elem + 2 * B * H * D * elem + B * H * 4
+    return 2 * vis * Hkv * D * elem + 2 * B * H * D * elem + B * H * 4
 
 
 def source_hash() -> str:
@@ -188,12 +191,15 @@ def bench_training(torch, swattn, inputs, cfg_name, steps, warmup, cold_steps=50
             "acct": step_accounting(B, H, T, D, windows)}
 
 
-def bench_decode(torch, swattn, inputs, iters):
+def bench_decode(torch, swattn, inputs, iters, hkv=None):
+    """Cold decode of the 32-sequence workload at each of its windows; with ``hkv`` the
+    same workload with that many K/V heads (grouped-query decode)."""
     c = inputs.CONFIGS["decode"]
-    d = inputs.config_inputs("decode")
+    B, H, D, Tmax = c["B"], c["H"], c["D"], c["Tmax"]
+    lengths = inputs.decode_lengths(B, c["len_seed"], c["len_lo"], c["len_hi"])
+    d = inputs.decode_inputs(B, H, D, Tmax, c["dtype"], c["seed"], lengths, Hkv=hkv)
     lengths = d["seqlens"].tolist()
     g = {n: t.to("cuda:0") for n, t in d.items()}
-    B, H, D, Tmax = c["B"], c["H"], c["D"], c["Tmax"]
     scale = 1.0 / math.sqrt(D)
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
     out = {}
@@ -202,9 +208,10 @@ def bench_decode(torch, swattn, inputs, iters):
                          device="cuda:0")
         o = torch.empty_like(g["q"])
         lse = torch.empty((B, H), dtype=torch.float32, device="cuda:0")
+        entry = swattn.swattn_decode if hkv is None else swattn.swattn_decode_gqa
 
         def call():
-            swattn.swattn_decode(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], o, lse, W, scale, ws)
+            entry(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], o, lse, W, scale, ws)
 
         for _ in range(3):
             call()
@@ -224,7 +231,7 @@ def bench_decode(torch, swattn, inputs, iters):
             b.record()
             torch.cuda.synchronize()
             warm.append(a.elapsed_time(b))
-        nbytes = decode_bytes(lengths, H, D, W)
+        nbytes = decode_bytes(lengths, H, D, W, Hkv=hkv)
         ms = statistics.median(cold)
         gbs = nbytes / (ms * 1e-3) / 1e9
         out["causal" if W < 0 else f"window{W}"] = {
@@ -233,6 +240,63 @@ def bench_decode(torch, swattn, inputs, iters):
             "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
         }
     return out
+
+
+def bench_training_gqa(torch, swattn, inputs, cfg_name, hkv, steps, warmup):
+    """The training workload with ``hkv`` K/V heads shared by its query heads in groups:
+    forward and backward of every layer through the grouped-query entry points (the
+    backward as one call: dQ, the per-head dK/dV pass and the group sum)."""
+    c = inputs.CONFIGS[cfg_name]
+    B, H, T, D = c["B"], c["H"], c["T"], c["D"]
+    scale = 1.0 / math.sqrt(D)
+    layers = []
+    for i, W in enumerate(c["windows"]):
+        x = {n: t.to("cuda:0") for n, t in inputs.training_inputs(
+            B, T, H, D, c["dtype"], c["seeds"][i], c["qk_norm"], Hkv=hkv).items()}
+        layers.append(dict(W=W, **x, o=torch.empty_like(x["q"]),
+                           lse=torch.empty((B, H, T), dtype=torch.float32, device="cuda:0"),
+                           dq=torch.empty_like(x["q"]), dk=torch.empty_like(x["k"]),
+                           dv=torch.empty_like(x["v"])))
+    ws = torch.empty(swattn.swattn_bwd_gqa_workspace_size(B, H, hkv, T, D), dtype=torch.uint8,
+                     device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for i, L in enumerate(layers):
+            if ev is not None:
+                ev[i][0].record(stream)
+            swattn.swattn_fwd_gqa(L["q"], L["k"], L["v"], L["o"], L["lse"], L["W"], scale)
+            if ev is not None:
+                ev[i][1].record(stream)
+        for i in reversed(range(len(layers))):
+            L = layers[i]
+            if ev is not None:
+                ev[i][2].record(stream)
+            swattn.swattn_bwd_gqa(L["q"], L["k"], L["v"], L["o"], L["do"], L["lse"], L["dq"],
+                                  L["dk"], L["dv"], L["W"], scale, ws)
+            if ev is not None:
+                ev[i][3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in layers]
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: statistics.fmean(sum(e[i][a].elapsed_time(e[i][b]) for i in range(len(layers)))
+                               for e in evs) for n, (a, b) in {"fwd": (0, 1), "bwd": (2, 3)}.items()}
+    acct = step_accounting(B, H, T, D, list(c["windows"]))
+    ms = wall / steps * 1e3
+    return {"workload": f"{cfg_name} with {hkv} K/V heads for {H} query heads",
+            "ms_per_step": round(ms, 4),
+            "TFLOP_per_s": round((acct["flops_fwd"] + acct["flops_bwd"]) / (ms * 1e-3) / 1e12, 2),
+            "fwd_ms": round(per["fwd"], 4), "bwd_ms": round(per["bwd"], 4),
+            "fwd_TFLOP_per_s": round(acct["flops_fwd"] / (per["fwd"] * 1e-3) / 1e12, 1),
+            "bwd_TFLOP_per_s": round(acct["flops_bwd"] / (per["bwd"] * 1e-3) / 1e12, 1)}
 
 
 def measured_refs(torch):
@@ -393,6 +457,9 @@ def main():
     ap.add_argument("--config", default="small", help="training workload (default: small)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hkv", type=int, default=0,
+                    help="also time the training workload with this many K/V heads "
+                         "(grouped-query entry points)")
     ap.add_argument("--no-refs", action="store_true",
                     help="skip the measured copy-bandwidth and GEMM references")
     ap.add_argument("--decode-iters", type=int, default=20)
@@ -475,6 +542,15 @@ def main():
     if not args.no_decode:
         res["decode"] = bench_decode(torch, swattn, inputs, args.decode_iters)
         log(f"decode {res['decode']}")
+        # grouped-query decode: the same 32 sequences with 4 K/V heads (3 query heads
+        # each) and with one (multi-query); bytes count the Hkv cache heads
+        res["decode_gqa"] = {f"hkv{n}": bench_decode(torch, swattn, inputs, args.decode_iters, n)
+                             for n in (4, 1)}
+        log(f"decode gqa {res['decode_gqa']}")
+    if args.hkv:
+        res["training_gqa"] = bench_training_gqa(torch, swattn, inputs, args.config, args.hkv,
+                                                 max(50, args.steps // 4), max(50, args.warmup // 2))
+        log(f"training gqa {res['training_gqa']}")
     if not args.no_refs:
         refs = measured_refs(torch)
         res["measured_refs"] = refs

@@ -49,6 +49,48 @@ __device__ __forceinline__ int visible_lo(int L, int window) {
   return window > 0 ? max(0, L - window) : 0;
 }
 
+// Reductions across the lanes of a wave without LDS: DPP within 16-lane rows
+// (quad_perm, row_half_mirror, row_mirror, row_ror) and permlane16/32 swaps between
+// rows.  group_sum<N>: sum over each aligned group of N lanes, in every lane of the
+// group.  across_groups_*<N>: over the lanes 64 / N apart that share a position in
+// their group (for max, a value constant within each group).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float swap16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16 || N == 32, "lanes per row");
+  x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]: lane ^ 1
+  x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+  x += dpp<0x141>(x);  // row_half_mirror: the other quad of the 8 (values equal per quad)
+  if constexpr (N >= 16) x += dpp<0x140>(x);  // row_mirror: the other 8 of the row
+  if constexpr (N >= 32) x = swap16_sum(x);
+  return x;
+}
+template <int N>
+__device__ __forceinline__ float across_groups_max(float x) {
+  if constexpr (N <= 8) x = fmaxf(x, dpp<0x140>(x));  // row_mirror: the other group of 8
+  if constexpr (N <= 16) x = swap16_max(x);
+  return xhalf_max(x);
+}
+template <int N>
+__device__ __forceinline__ float across_groups_sum(float x) {
+  if constexpr (N <= 8) x += dpp<0x128>(x);  // row_ror 8: lane ^ 8 within the row
+  if constexpr (N <= 16) x = swap16_sum(x);
+  return xhalf_sum(x);
+}
+
 // GROUPED: more than one query head per K/V head (H > Hkv).  Without it the head loop
 // has one trip known at compile time, and the K/V rows need not stay in registers
 // after their use.
@@ -64,10 +106,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   constexpr int CH = kDecodeChunk;      // rows per workgroup
   constexpr int TPW = CH / 4;           // rows per wave
   constexpr int ROUNDS = TPW / GPW;
-  __shared__ float part_o[4][D];
-  __shared__ float part_ml[4][2];
+  constexpr int GB = GROUPED ? kDecodeHeadBatch : 1;  // query heads merged per batch
+  __shared__ float part_o[4][GB][D];
+  __shared__ float part_ml[4][GB][2];
 
-  // heads vary fastest across workgroups: the workgroups reading the rows of one
+  // K/V heads vary fastest across workgroups: the workgroups reading the rows of one
   // token range (adjacent 256-byte pieces of the same cache lines' DRAM pages) run together
   const int hk = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
   const int G = GROUPED ? H / Hkv : 1;  // query heads hk * G .. hk * G + G - 1 read K/V head hk
@@ -88,6 +131,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   if (c * CH >= n) return;
   const int t0 = lo + c * CH;
   const int cnt = min(CH, L - t0);
+  const int nch = (n + CH - 1) / CH;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int grp = lane / LPR, sl = lane % LPR;
@@ -108,85 +152,93 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const int t = min(w * TPW + r * GPW + grp, cnt - 1);
     vr[r] = ldg16_stream(vb + (size_t)(t0 + t) * rs);
   }
-  // the query heads of the group in turn; each one's q row is requested one head ahead
+  // scores in exp2 units: q is scaled by scale * log2(e)
+  const float qs = scale * kLog2e;
   const TT *qg = q + ((size_t)b * H + hk * G) * D + sl * EPL;
-  u32x4 qraw = ldg16(qg);
-  const size_t slot0 = ((size_t)b * H + hk * G) * nsplit + c;
-  const int nch = (n + CH - 1) / CH;
-  for (int g = 0; g < G; ++g) {
-    const int bh = b * H + hk * G + g;
-    const u32x4 qnext = g + 1 < G ? ldg16(qg + (size_t)(g + 1) * D) : qraw;
-    float qf[EPL];
-    Elem<TT>::unpack(qraw, qf);
-    qraw = qnext;
+  u32x4 qraw = ldg16(qg);  // each query head's q row is requested one head ahead
 
-    // scores of this wave's rows (each lane group holds one row per round)
-    float sc[ROUNDS];
-    float m = -INFINITY;
+  for (int g0 = 0; g0 < G; g0 += GB) {
+    const int gn = min(GB, G - g0);
+    // each query head of the batch in turn: this wave's share of (m, l, o) into LDS
+    for (int j = 0; j < gn; ++j) {
+      const int g = g0 + j;
+      const u32x4 qnext = g + 1 < G ? ldg16(qg + (size_t)(g + 1) * D) : qraw;
+      float qf[EPL];
+      Elem<TT>::unpack(qraw, qf);
+      qraw = qnext;
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
-      float kf[EPL];
-      Elem<TT>::unpack(kr[r], kf);
-      float dot = 0.f;
+      for (int e = 0; e < EPL; ++e) qf[e] *= qs;
+
+      // scores of this wave's rows (each lane group holds one row per round)
+      float sc[ROUNDS];
+      float m = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], kf[e], dot);
+      for (int r = 0; r < ROUNDS; ++r) {
+        float kf[EPL];
+        Elem<TT>::unpack(kr[r], kf);
+        float dot = 0.f;
 #pragma unroll
-      for (int off = LPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, LPR);
-      const bool ok = w * TPW + r * GPW + grp < cnt;
-      sc[r] = ok ? dot * scale : -INFINITY;
-      m = fmaxf(m, sc[r]);
-    }
+        for (int e = 0; e < EPL; ++e) dot = fmaf(qf[e], kf[e], dot);
+        dot = group_sum<LPR>(dot);
+        const bool ok = w * TPW + r * GPW + grp < cnt;
+        sc[r] = ok ? dot : -INFINITY;
+        m = fmaxf(m, sc[r]);
+      }
+      m = across_groups_max<LPR>(m);
+      const float mu = m == -INFINITY ? 0.f : m;
+      float lsum = 0.f, acc[EPL];
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-    const float mu = m == -INFINITY ? 0.f : m;
-    float lsum = 0.f, acc[EPL];
+      for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+      for (int r = 0; r < ROUNDS; ++r) {
+        const float p = fast_exp2(sc[r] - mu);
+        lsum += p;
+        float vf[EPL];
+        Elem<TT>::unpack(vr[r], vf);
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
-      const float p = expf(sc[r] - mu);
-      lsum += p;
-      float vf[EPL];
-      Elem<TT>::unpack(vr[r], vf);
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+      }
+      // sum over the lane groups of the wave (lanes with the same sl)
+      lsum = across_groups_sum<LPR>(lsum);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
-    }
-    // sum over the lane groups of the wave
+      for (int e = 0; e < EPL; ++e) acc[e] = across_groups_sum<LPR>(acc[e]);
+      if (grp == 0) {
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) {
-      lsum += __shfl_xor(lsum, off);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], off);
-    }
-    if (grp == 0) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) part_o[w][sl * EPL + e] = acc[e];
-      if (sl == 0) {
-        part_ml[w][0] = m;
-        part_ml[w][1] = lsum;
+        for (int e = 0; e < EPL; ++e) part_o[w][j][sl * EPL + e] = acc[e];
+        if (sl == 0) {
+          part_ml[w][j][0] = m;
+          part_ml[w][j][1] = lsum;
+        }
       }
     }
     __syncthreads();
-    // merge the four wave partials (a wave without visible rows has m = -inf, l = 0)
-    const float M = fmaxf(fmaxf(part_ml[0][0], part_ml[1][0]), fmaxf(part_ml[2][0], part_ml[3][0]));
-    float f[4], Ltot = 0.f;
+    // merge the four wave partials of each head (a wave without visible rows has
+    // m = -inf, l = 0); m is in exp2 units, lse in natural log
+    for (int i = tid; i < gn * D; i += 256) {
+      const int j = i / D, d = i % D;
+      const int bh = b * H + hk * G + g0 + j;
+      float M = part_ml[0][j][0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[i] = part_ml[i][0] == -INFINITY ? 0.f : expf(part_ml[i][0] - M);
-      Ltot += f[i] * part_ml[i][1];
+      for (int u = 1; u < 4; ++u) M = fmaxf(M, part_ml[u][j][0]);
+      float f[4], Ltot = 0.f, ov = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        f[u] = part_ml[u][j][0] == -INFINITY ? 0.f : fast_exp2(part_ml[u][j][0] - M);
+        Ltot += f[u] * part_ml[u][j][1];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ov += f[u] * part_o[u][j][d];
+      ov /= Ltot;
+      const size_t slot = (size_t)bh * nsplit + c;
+      if (nch == 1) o[(size_t)bh * D + d] = Elem<TT>::pack(ov);  // nothing to merge
+      else ws_o[slot * D + d] = ov;
+      if (d == 0) {
+        const float l = M * kLn2 + logf(Ltot);
+        if (nch > 1) ws_lse[slot] = l;
+        else if (lse) lse[bh] = l;
+      }
     }
-    const size_t slot = slot0 + (size_t)g * nsplit;
-    if (tid < D) {
-      const float ov = (f[0] * part_o[0][tid] + f[1] * part_o[1][tid] + f[2] * part_o[2][tid] +
-                        f[3] * part_o[3][tid]) / Ltot;
-      if (nch == 1) o[(size_t)bh * D + tid] = Elem<TT>::pack(ov);  // nothing to merge
-      else ws_o[slot * D + tid] = ov;
-    }
-    if (tid == 0) {
-      if (nch > 1) ws_lse[slot] = M + logf(Ltot);
-      else if (lse) lse[bh] = M + logf(Ltot);
-    }
-    __syncthreads();  // part_o / part_ml are written again for the next query head
+    __syncthreads();  // part_o / part_ml are written again for the next batch
   }
 }
 

@@ -8,6 +8,9 @@ namespace swattn {
 
 // Number of KV rows one decode workgroup handles.
 constexpr int kDecodeChunk = 128;
+// Query heads whose partials a grouped decode workgroup merges together (its LDS holds
+// four wave partials of each).
+constexpr int kDecodeHeadBatch = 16;
 
 int decode_num_splits(int Tmax, int window);
 
