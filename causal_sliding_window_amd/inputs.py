@@ -40,6 +40,11 @@ CONFIGS = {
                     qk_norm=True),
     "wide-sw": dict(kind="train", B=2, H=16, T=4096, D=128, dtype="bf16",
                     windows=[256], seeds=[0], qk_norm=True),
+    # the guide's "SSSL" layer pattern (three short-window layers, then one long) at the
+    # mid model's shape; the pages give no window sizes: short = T / 4 (as mid-alt's
+    # short layers), long = full causal
+    "sssl": dict(kind="train", B=4, H=12, T=2048, D=128, dtype="bf16",
+                 windows=[512, 512, 512, 2048], seeds=[0, 4, 8, 12], qk_norm=True),
     "decode": dict(kind="decode", B=32, H=12, D=128, Tmax=4096, dtype="bf16",
                    windows=[-1, 1024], len_seed=7, len_lo=512, len_hi=4096,
                    seed=7),

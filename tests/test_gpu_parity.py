@@ -14,7 +14,7 @@ import torch
 
 from causal_sliding_window_amd import inputs, swattn
 from oracle import attention as orc
-from parity import check, f64, only_heads
+from parity import check, f64, only_heads, sample_heads
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -168,6 +168,26 @@ def test_mid_alt_layer_schedule_all_heads():
 
 
 # ----------------------------------------------------------------------------- decode
+def test_sssl_layer_schedule_sampled():
+    """The "SSSL" pattern (windows 512, 512, 512, 2048) at the mid model's shape: forwards
+    0..3 then backwards 3..0 on one stream, as the benchmark runs it; every layer
+    compared on sampled heads."""
+    c = inputs.CONFIGS["sssl"]
+    scale = 1 / math.sqrt(c["D"])
+    xs = [inputs.config_inputs("sssl", layer) for layer in range(4)]
+    gs = [_gpu(x) for x in xs]
+    fw = [swattn.fwd(g["q"], g["k"], g["v"], c["windows"][i], scale) for i, g in enumerate(gs)]
+    bw = [None] * 4
+    for layer in (3, 2, 1, 0):
+        g, (o, lse) = gs[layer], fw[layer]
+        bw[layer] = swattn.bwd(g["q"], g["k"], g["v"], o, g["do"], lse, c["windows"][layer], scale)
+    torch.cuda.synchronize()
+    heads = sample_heads(c["B"], c["H"], 3, seed=11)
+    for layer in range(4):
+        ref = oracle_fwd_bwd(xs[layer], c["windows"][layer], scale, heads)
+        compare_all(fw[layer] + bw[layer], ref, torch.bfloat16, heads, f"layer{layer} ")
+
+
 def _decode_oracle(d, W, scale):
     a = {n: inputs.to_f64(d[n]) for n in ("q", "k_cache", "v_cache")}
     return orc.attn_decode(a["q"], a["k_cache"], a["v_cache"], d["seqlens"].numpy(), W, scale)
