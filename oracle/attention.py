@@ -28,6 +28,12 @@ Readings where the pages are silent:
   q, k, v (LSE is an output only; nothing flows back through it).
 * Decode: ``seqlens[b] = L`` counts valid cache rows including the new token; the
   query sits at position ``L - 1``.  ``L == 0`` gives o = 0, LSE = -inf.
+* Prefill with cache append (same section 6: the engine fills the cache through the
+  kernels' with-KV-cache entry; one chunk of Tq new tokens at a time): with
+  ``L0 = seqlens[b]`` rows already cached, the chunk's K/V rows are written at rows
+  ``L0 .. L0 + Tq - 1`` and query i sits at position ``L0 + i``.  ``seqlens`` is
+  clamped to ``[0, Tmax - Tq]`` so that every written row exists (the reading for
+  a length the pages leave unbounded).
 * Grouped-query attention (same guide, section 1 feature list: fewer K/V heads than
   query heads, for faster inference; the multi-query case, one K/V head, is in the
   architecture list of the release article).  The pages do not say which query
@@ -51,6 +57,7 @@ __all__ = [
     "attn_fwd",
     "attn_bwd",
     "attn_decode",
+    "attn_prefill",
 ]
 
 
@@ -224,3 +231,35 @@ def attn_decode(q, k_cache, v_cache, seqlens, window: int, scale: float,
             o[b, h] = (p @ vb)[0]
             lse[b, h] = l_[0]
     return o, lse
+
+
+def attn_prefill(q, k_new, v_new, k_cache, v_cache, seqlens, window: int, scale: float):
+    """Chunked prefill against a KV cache, appending the chunk's K/V first.
+
+    q: [B, Tq, H, D]; k_new, v_new: [B, Tq, Hkv, D]; k_cache, v_cache: [B, Tmax, Hkv, D];
+    seqlens: [B] ints, the cache rows already filled.  For sequence b, with
+    L0 = min(max(seqlens[b], 0), Tmax - Tq), rows L0 .. L0 + Tq - 1 of copies of the
+    caches receive k_new[b], v_new[b]; query i then attends, as position L0 + i, to
+    the rows of the updated cache that :func:`visible_mask` allows (rows past
+    L0 + i are never visible).  Returns (o [B, Tq, H, D], lse [B, H, Tq], k_cache',
+    v_cache').
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Tq, H, D = q.shape
+    G = _group(H, k_cache)
+    Tmax = k_cache.shape[1]
+    if Tq > Tmax:
+        raise ValueError(f"a chunk of {Tq} rows does not fit a cache of {Tmax}")
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    o = np.zeros((B, Tq, H, D))
+    lse = np.zeros((B, H, Tq))
+    for b in range(B):
+        L0 = min(max(int(seqlens[b]), 0), Tmax - Tq)
+        kc[b, L0:L0 + Tq] = k_new[b]
+        vc[b, L0:L0 + Tq] = v_new[b]
+        for h in range(H):
+            kb, vb = kc[b, :L0 + Tq, h // G, :], vc[b, :L0 + Tq, h // G, :]
+            p, lse[b, h] = head_probs(q[b, :, h, :], kb, window, scale, q_pos0=L0)
+            o[b, :, h, :] = p @ vb
+    return o, lse, kc, vc

@@ -434,3 +434,71 @@ def test_gqa_rejects_uneven_groups():
     q, k = _rand(1, 4, 6, 2), _rand(1, 4, 4, 2)
     with pytest.raises(ValueError):
         orc.attn_fwd(q, k, k, -1, 1.0)
+
+
+# ----------------------------------------------------------------------------- prefill
+def _prefill_case(B=2, Tq=5, H=4, Hkv=2, D=6, Tmax=20):
+    return (_rand(B, Tq, H, D), _rand(B, Tq, Hkv, D), _rand(B, Tq, Hkv, D),
+            _rand(B, Tmax, Hkv, D), _rand(B, Tmax, Hkv, D))
+
+
+@pytest.mark.parametrize("W", [-1, 1, 3, 8])
+def test_prefill_on_empty_cache_is_the_forward(W):
+    q, kn, vn, kc, vc = _prefill_case()
+    o, lse, kc2, vc2 = orc.attn_prefill(q, kn, vn, kc, vc, [0, 0], W, 0.4)
+    fo, fl = orc.attn_fwd(q, kn, vn, W, 0.4)
+    np.testing.assert_allclose(o, fo, atol=1e-13)
+    np.testing.assert_allclose(lse, fl, atol=1e-13)
+    np.testing.assert_array_equal(kc2[:, :5], kn)
+    np.testing.assert_array_equal(kc2[:, 5:], kc[:, 5:])  # rows past the chunk untouched
+
+
+@pytest.mark.parametrize("W", [-1, 4])
+def test_prefill_in_two_chunks_is_the_forward_of_the_whole(W):
+    """Chunk 1 at an empty cache, then chunk 2 at seqlens = len(chunk 1): the second
+    chunk's outputs are the last rows of the forward over both chunks."""
+    B, H, Hkv, D, Tmax = 2, 4, 2, 6, 16
+    q = _rand(B, 9, H, D)
+    k, v = _rand(B, 9, Hkv, D), _rand(B, 9, Hkv, D)
+    kc, vc = np.zeros((B, Tmax, Hkv, D)), np.zeros((B, Tmax, Hkv, D))
+    _, _, kc, vc = orc.attn_prefill(q[:, :4], k[:, :4], v[:, :4], kc, vc, [0, 0], W, 0.5)
+    o2, l2, _, _ = orc.attn_prefill(q[:, 4:], k[:, 4:], v[:, 4:], kc, vc, [4, 4], W, 0.5)
+    fo, fl = orc.attn_fwd(q, k, v, W, 0.5)
+    np.testing.assert_allclose(o2, fo[:, 4:], atol=1e-13)
+    np.testing.assert_allclose(l2, fl[:, :, 4:], atol=1e-13)
+
+
+@pytest.mark.parametrize("W", [-1, 2, 6])
+def test_prefill_last_row_is_decode_on_the_updated_cache(W):
+    q, kn, vn, kc, vc = _prefill_case()
+    seq = np.array([3, 11])
+    o, lse, kc2, vc2 = orc.attn_prefill(q, kn, vn, kc, vc, seq, W, 0.7)
+    od, ld = orc.attn_decode(q[:, -1], kc2, vc2, seq + 5, W, 0.7)
+    np.testing.assert_allclose(o[:, -1], od, atol=1e-13)
+    np.testing.assert_allclose(lse[:, :, -1], ld, atol=1e-13)
+
+
+def test_prefill_matches_torch_sdpa_offset_mask():
+    """An independent routine: SDPA (fp64) over the updated cache with the offset causal
+    and window mask built here, K/V heads repeated per group."""
+    q, kn, vn, kc, vc = _prefill_case(Tq=6, Tmax=24)
+    W, scale, seq = 5, 0.6, [7, 2]
+    o, lse, kc2, vc2 = orc.attn_prefill(q, kn, vn, kc, vc, seq, W, scale)
+    for b, L0 in enumerate(seq):
+        n = L0 + 6
+        i = np.arange(6)[:, None] + L0
+        j = np.arange(n)[None, :]
+        mask = torch.tensor((j <= i) & (i - j < W))
+        t = lambda a: torch.tensor(a).permute(1, 0, 2)  # noqa: E731  [T, h, D] -> [h, T, D]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            t(q[b]), t(kc2[b, :n]), t(vc2[b, :n]), attn_mask=mask, scale=scale, enable_gqa=True)
+        np.testing.assert_allclose(o[b], ref.permute(1, 0, 2).numpy(), atol=1e-12)
+
+
+def test_prefill_clamps_seqlens_to_the_cache():
+    q, kn, vn, kc, vc = _prefill_case(Tmax=12)
+    o, lse, kc2, _ = orc.attn_prefill(q, kn, vn, kc, vc, [30, -3], -1, 0.5)
+    o7, l7, kc7, _ = orc.attn_prefill(q, kn, vn, kc, vc, [7, 0], -1, 0.5)  # 12 - 5 = 7
+    np.testing.assert_array_equal(o, o7)
+    np.testing.assert_array_equal(kc2, kc7)
+    np.testing.assert_array_equal(kc2[0, 7:12], kn[0])
