@@ -242,6 +242,48 @@ def bench_decode(torch, swattn, inputs, iters, hkv=None):
     return out
 
 
+def bench_prefill(torch, swattn, inputs, iters, tq=512):
+    """Chunked prefill on the decode workload's caches: each of the 32 sequences appends a
+    chunk of ``tq`` tokens at (its decode length - tq) and attends the chunk's queries to
+    its cache, full causal.  Cold (a 1 GiB fill before each call); TFLOP/s counts the
+    visible (query, key) pairs, 4*D per pair."""
+    c = inputs.CONFIGS["decode"]
+    B, H, D, Tmax = c["B"], c["H"], c["D"], c["Tmax"]
+    lens = [max(int(L) - tq, 0) for L in inputs.decode_lengths(B, c["len_seed"], c["len_lo"],
+                                                                c["len_hi"])]
+    d = inputs.decode_inputs(B, H, D, Tmax, c["dtype"], c["seed"], lens)
+    x = inputs.training_inputs(B, tq, H, D, c["dtype"], seed=c["seed"] + 10)
+    g = {n: t.to("cuda:0") for n, t in d.items()}
+    q, kn, vn = (x[n].to("cuda:0") for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, tq), dtype=torch.float32, device="cuda:0")
+    scale = 1.0 / math.sqrt(D)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+
+    def call():
+        swattn.swattn_prefill(q, kn, vn, g["k_cache"], g["v_cache"], g["seqlens"], o, lse, -1,
+                              scale)
+
+    for _ in range(3):
+        call()
+    ts = []
+    for _ in range(iters):
+        flush.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    del flush
+    pairs = H * sum(tq * L0 + tq * (tq + 1) // 2 for L0 in lens)
+    ms = statistics.median(ts)
+    return {"workload": f"{B} sequences, H{H} D{D}, chunks of {tq} tokens appended at "
+                        f"(decode length - {tq}), cache of {Tmax} rows, full causal",
+            "us_cold_median": round(ms * 1e3, 2),
+            "TFLOP_per_s": round(4 * D * pairs / (ms * 1e-3) / 1e12, 1)}
+
+
 def bench_training_gqa(torch, swattn, inputs, cfg_name, hkv, steps, warmup):
     """The training workload with ``hkv`` K/V heads shared by its query heads in groups:
     forward and backward of every layer through the grouped-query entry points (the
@@ -547,6 +589,8 @@ def main():
         res["decode_gqa"] = {f"hkv{n}": bench_decode(torch, swattn, inputs, args.decode_iters, n)
                              for n in (4, 1)}
         log(f"decode gqa {res['decode_gqa']}")
+        res["prefill"] = bench_prefill(torch, swattn, inputs, args.decode_iters)
+        log(f"prefill {res['prefill']}")
     if args.hkv:
         res["training_gqa"] = bench_training_gqa(torch, swattn, inputs, args.config, args.hkv,
                                                  max(50, args.steps // 4), max(50, args.warmup // 2))

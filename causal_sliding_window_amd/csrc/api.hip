@@ -262,6 +262,24 @@ int swattn_bwd_dq_f32(const float *q, const float *k, const float *v, const floa
                 (hipStream_t)stream);
 }
 
+int swattn_prefill(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                   void *v_cache, const int *seqlens, void *o, float *lse, int B, int H,
+                   int Hkv, int Tq, int D, int Tmax, int window, float scale,
+                   swattn_stream_t stream) {
+  int st = check_common(B, H, Tq, D, window);
+  if (st == SWATTN_OK) st = check_group(H, Hkv);
+  if (st != SWATTN_OK) return st;
+  if (Tmax <= 0 || Tq > Tmax) return SWATTN_ERR_INVALID_ARG;
+  // the caches: 32-bit grid/row indices and 32-bit buffer offsets per sequence
+  if ((long long)B * Tmax * Hkv > INT_MAX / 2) return SWATTN_ERR_INVALID_ARG;
+  if ((long long)(Tmax + 128) * Hkv * D * 2 > INT_MAX) return SWATTN_ERR_UNSUPPORTED;
+  if (!all_aligned({q, k_new, v_new, k_cache, v_cache, o}) || seqlens == nullptr)
+    return SWATTN_ERR_INVALID_ARG;
+  return hip_status(swattn::launch_prefill_bf16(q, k_new, v_new, k_cache, v_cache, seqlens, o,
+                                                lse, B, H, Hkv, Tq, D, Tmax, window, scale,
+                                                (hipStream_t)stream));
+}
+
 size_t swattn_decode_workspace_size(int B, int H, int D, int Tmax, int window) {
   if (check_decode(B, H, D, Tmax, window) != SWATTN_OK) return 0;
   const size_t ns = (size_t)swattn::decode_num_splits(Tmax, window);

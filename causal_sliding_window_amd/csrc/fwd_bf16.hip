@@ -21,6 +21,14 @@
 //     lower edge;
 //   * the unmasked loop is aligned so that its two steps always use the same LDS
 //     slots: every operand address is then a lane offset plus a constant.
+//
+// The same kernel serves chunked prefill (PREFILL): T query rows of a sequence sit at
+// positions off .. off + T - 1 of a KV cache of Tkv rows, which already holds the
+// chunk's own K/V rows (cache_append_kernel runs first), with off = seqlens[b] read
+// on the device and clamped to [0, Tkv - T].  Band, masks and tiles work in absolute
+// positions; q, o and lse are indexed within the chunk.  With off not a multiple of
+// 32 a wave's diagonal spans two key tiles, so every tile from the first one the
+// diagonal touches runs the element mask.
 #include <type_traits>
 
 #include "common.h"
@@ -42,11 +50,12 @@ struct FwdCfg {
 // Row-max growth (exp2 units) tolerated before the running max is moved.
 constexpr float kRescaleLog2 = 8.f;
 
-template <int D>
+template <int D, bool PREFILL>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
-    int B, int H, int Hkv, int T, int window, float scale, int nqt) {
+    const int *__restrict__ seqlens, int B, int H, int Hkv, int T, int Tkv, int window,
+    float scale, int nqt) {
   using C = FwdCfg<D>;
   // [slot][K, V][TSZ]
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * C::TSZ];
@@ -56,12 +65,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int qt = nqt - 1 - bid / BH;  // longest (latest) query tiles first
   const int bh = bid % BH;            // consecutive blocks: different heads
   const int b = bh / H, hh = bh % H;
-  const int q0 = qt * C::BM;
+  // positions of the chunk's queries start at off; keys 0 .. Tk - 1 are in view
+  const int off = PREFILL ? min(max(seqlens[b], 0), Tkv - T) : 0;
+  const int Tk = off + T;
+  const int q0 = off + qt * C::BM;
   const int rs = H * D;                // row stride of q and o (elements)
   const int rsk = Hkv * D;             // row stride of k and v
   const int hk = hh / (H / Hkv);       // the K/V head of query head hh
   const size_t base = ((size_t)b * T * H + hh) * D;
-  const size_t base_kv = ((size_t)b * T * Hkv + hk) * D;
+  const size_t base_kv = ((size_t)b * Tkv * Hkv + hk) * D;
   const uint16_t *qb = q + base, *kb = k + base_kv, *vb = v + base_kv;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -71,15 +83,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int my_q = qw0 + ln;
 
   // key tiles of the workgroup and of this wave
-  const int q_last = min(T, q0 + C::BM) - 1;
+  const int q_last = min(Tk, q0 + C::BM) - 1;
   const int k_lo = window > 0 ? max(0, q0 - window + 1) : 0;
   const int kt0 = k_lo / C::BN, kt1 = q_last / C::BN;
   int wkt0 = 1 << 30, wkt1 = -1;
-  if (qw0 < T) {
+  if (qw0 < Tk) {
     wkt0 = (window > 0 ? max(0, qw0 - window + 1) : 0) / C::BN;
-    wkt1 = min(T - 1, qw0 + 31) / C::BN;
+    wkt1 = min(Tk - 1, qw0 + 31) / C::BN;
   }
-  const int wq_lo = qw0, wq_hi = min(T - 1, qw0 + 31);
+  const int wq_lo = qw0, wq_hi = min(Tk - 1, qw0 + 31);
   // key kk is visible to my_q iff 0 <= my_q - kk <= wm1
   const unsigned wm1 = window > 0 ? (unsigned)(window - 1) : 0x7fffffffu;
 
@@ -90,7 +102,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 #pragma unroll
     for (int st = 0; st < C::KST; ++st)
       qr[st] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, (my_q * rs + 16 * st + 8 * h) * 2, 0, 0));
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, ((my_q - off) * rs + 16 * st + 8 * h) * 2,
+                                                        0, 0));
   }
 
   // Copy j of a tile (1 KB): LDS block db = j / RG, rows 16 (j % RG) .. + 15.
@@ -103,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t *src = tensor ? vb : kb;
     const int row0 = kt * C::BN;
     const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(src + (size_t)row0 * rsk, (uint32_t)(T - row0) * rsk * 2);
+        make_rsrc(src + (size_t)row0 * rsk, (uint32_t)(Tk - row0) * rsk * 2);
     uint16_t *tile = smem + (2 * slot + tensor) * C::TSZ;
 #pragma unroll
     for (int cc = 0; cc < C::CPW; ++cc) {
@@ -306,9 +319,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     sc = sn;
     sync();
   }
+  // Tiles from ulim on hold keys past some query of the wave (only the diagonal tile
+  // wkt1 when the wave's queries start on a tile boundary).
+  const int ulim = PREFILL ? min(wkt1, (qw0 + 1) / C::BN) : wkt1;
   // unmasked tiles, two per iteration: S of the next tile alternates between sc and
   // sn, so no registers are copied
-  if (kt + 1 < wkt1 && ((kt - kt0) & 1)) {  // align the pair loop to slot 0
+  if (kt + 1 < ulim && ((kt - kt0) & 1)) {  // align the pair loop to slot 0
     step(std::false_type{}, [&] { loads(kt); }, k_next(kt), v_cur(kt), kt * C::BN, sc, sn);
     sc = sn;
     sync();
@@ -316,7 +332,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   }
   // (kt - kt0) is even here: the slots of both steps are fixed, so every LDS address
   // is a loop-invariant lane offset plus a constant
-  for (; kt + 1 < wkt1; kt += 2) {
+  for (; kt + 1 < ulim; kt += 2) {
     step(std::false_type{}, [&] { loads(kt); }, smem + 2 * C::TSZ, smem + C::TSZ, kt * C::BN, sc,
          sn);
     sync();
@@ -324,11 +340,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
          sc);
     sync();
   }
-  if (kt < wkt1) {
+  if (kt < ulim) {
     step(std::false_type{}, [&] { loads(kt); }, k_next(kt), v_cur(kt), kt * C::BN, sc, sn);
     sc = sn;
     sync();
     ++kt;
+  }
+  if constexpr (PREFILL) {
+    for (; kt < wkt1; ++kt) {  // tiles before the last one that the diagonal crosses
+      step(std::true_type{}, [&] { loads(kt); }, k_next(kt), v_cur(kt), kt * C::BN, sc, sn);
+      sc = sn;
+      sync();
+    }
   }
   if (kt == wkt1) {  // the diagonal tile: no S to compute ahead
     VOps va;
@@ -348,9 +371,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   }
 
   const float l_tot = xhalf_sum(l_run);
-  if (my_q < T) {
+  if (my_q < Tk) {
     const float inv = 1.f / l_tot;
-    uint16_t *orow = o + base + (size_t)my_q * rs;
+    uint16_t *orow = o + base + (size_t)(my_q - off) * rs;
 #pragma unroll
     for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
@@ -360,7 +383,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[d][4 * g + e] * inv);
         *reinterpret_cast<bf16x4 *>(orow + 32 * d + 8 * g + 4 * h) = pk;
       }
-    if (h == 0) lse[(size_t)bh * T + my_q] = m_run * scale + logf(l_tot);
+    if (h == 0 && (!PREFILL || lse != nullptr))
+      lse[(size_t)bh * T + (my_q - off)] = m_run * scale + logf(l_tot);
   }
 }
 
@@ -370,13 +394,52 @@ hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o,
   const int nqt = (T + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
   dim3 grid((unsigned)(nqt * B * H)), block(256);
   if (D == 128)
-    fwd_bf16_kernel<128><<<grid, block, 0, st>>>((const uint16_t *)q, (const uint16_t *)k,
-                                                 (const uint16_t *)v, (uint16_t *)o, lse, B, H,
-                                                 Hkv, T, window, scale, nqt);
+    fwd_bf16_kernel<128, false><<<grid, block, 0, st>>>(
+        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr,
+        B, H, Hkv, T, T, window, scale, nqt);
   else
-    fwd_bf16_kernel<64><<<grid, block, 0, st>>>((const uint16_t *)q, (const uint16_t *)k,
-                                                (const uint16_t *)v, (uint16_t *)o, lse, B, H,
-                                                Hkv, T, window, scale, nqt);
+    fwd_bf16_kernel<64, false><<<grid, block, 0, st>>>(
+        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr,
+        B, H, Hkv, T, T, window, scale, nqt);
+  return hipGetLastError();
+}
+
+// Rows t of the chunk go to cache rows off_b + t, off_b = seqlens[b] clamped to
+// [0, Tmax - Tq] (the same clamp as the prefill forward); 8 elements per thread.
+__global__ __launch_bounds__(256) void cache_append_kernel(
+    const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+    uint16_t *__restrict__ k_cache, uint16_t *__restrict__ v_cache,
+    const int *__restrict__ seqlens, int Tq, int Hkv, int D, int Tmax, long long n8) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const long long e = i * 8;               // element of k_new: ((b Tq + t) Hkv + hk) D + d
+  const long long row = e / D, d = e % D;  // row = (b Tq + t) Hkv + hk
+  const long long hk = row % Hkv, bt = row / Hkv;
+  const long long t = bt % Tq, b = bt / Tq;
+  const int off = min(max(seqlens[b], 0), Tmax - Tq);
+  const long long dst = ((b * Tmax + off + t) * Hkv + hk) * D + d;
+  *reinterpret_cast<u32x4 *>(k_cache + dst) = *reinterpret_cast<const u32x4 *>(k_new + e);
+  *reinterpret_cast<u32x4 *>(v_cache + dst) = *reinterpret_cast<const u32x4 *>(v_new + e);
+}
+
+hipError_t launch_prefill_bf16(const void *q, const void *k_new, const void *v_new,
+                               void *k_cache, void *v_cache, const int *seqlens, void *o,
+                               float *lse, int B, int H, int Hkv, int Tq, int D, int Tmax,
+                               int window, float scale, hipStream_t st) {
+  const long long n8 = (long long)B * Tq * Hkv * D / 8;
+  cache_append_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(
+      (const uint16_t *)k_new, (const uint16_t *)v_new, (uint16_t *)k_cache,
+      (uint16_t *)v_cache, seqlens, Tq, Hkv, D, Tmax, n8);
+  const int nqt = (Tq + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
+  dim3 grid((unsigned)(nqt * B * H)), block(256);
+  if (D == 128)
+    fwd_bf16_kernel<128, true><<<grid, block, 0, st>>>(
+        (const uint16_t *)q, (const uint16_t *)k_cache, (const uint16_t *)v_cache, (uint16_t *)o,
+        lse, seqlens, B, H, Hkv, Tq, Tmax, window, scale, nqt);
+  else
+    fwd_bf16_kernel<64, true><<<grid, block, 0, st>>>(
+        (const uint16_t *)q, (const uint16_t *)k_cache, (const uint16_t *)v_cache, (uint16_t *)o,
+        lse, seqlens, B, H, Hkv, Tq, Tmax, window, scale, nqt);
   return hipGetLastError();
 }
 

@@ -19,6 +19,12 @@ int decode_num_splits(int Tmax, int window);
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                            int B, int H, int Hkv, int T, int D, int window, float scale,
                            hipStream_t st);
+// Chunked prefill: appends the chunk's K/V rows to the caches at seqlens[b] (clamped to
+// [0, Tmax - Tq]), then runs the forward for its Tq queries against the caches.
+hipError_t launch_prefill_bf16(const void *q, const void *k_new, const void *v_new,
+                               void *k_cache, void *v_cache, const int *seqlens, void *o,
+                               float *lse, int B, int H, int Hkv, int Tq, int D, int Tmax,
+                               int window, float scale, hipStream_t st);
 hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                           int B, int H, int T, int D, int window, float scale, hipStream_t st);
 

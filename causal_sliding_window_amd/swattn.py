@@ -49,6 +49,7 @@ _SIGS = {
     "swattn_bwd_gqa_workspace_size": ([_I] * 5, ctypes.c_size_t),
     "swattn_bwd_gqa": ([_P] * 9 + [_I] * 6 + [_F, _P, _P], _I),
     "swattn_decode_gqa": ([_P] * 6 + [_I] * 6 + [_F, _P, _P], _I),
+    "swattn_prefill": ([_P] * 8 + [_I] * 7 + [_F, _P], _I),
 }
 
 
@@ -290,6 +291,28 @@ def swattn_decode_gqa(q, k_cache, v_cache, seqlens, o, lse, window: int, scale: 
            "swattn_decode_gqa")
 
 
+def swattn_prefill(q, k_new, v_new, k_cache, v_cache, seqlens, o, lse, window: int,
+                   scale: float, stream=None):
+    """Chunked prefill (bf16): appends k_new, v_new [B,Tq,Hkv,D] to the caches [B,Tmax,Hkv,D]
+    at seqlens (clamped to [0, Tmax - Tq]) and attends q [B,Tq,H,D] against them into o
+    (and lse [B,H,Tq] unless None)."""
+    B, Tq, H, D = q.shape
+    Tmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _groups(H, Hkv)
+    for n, t, shape in (("q", q, (B, Tq, H, D)), ("o", o, (B, Tq, H, D)),
+                        ("k_new", k_new, (B, Tq, Hkv, D)), ("v_new", v_new, (B, Tq, Hkv, D)),
+                        ("k_cache", k_cache, (B, Tmax, Hkv, D)),
+                        ("v_cache", v_cache, (B, Tmax, Hkv, D))):
+        _dev_tensor(t, n, torch.bfloat16, shape)
+    _dev_tensor(seqlens, "seqlens", torch.int32, (B,))
+    if lse is not None:
+        _dev_tensor(lse, "lse", torch.float32, (B, H, Tq))
+    _check(lib().swattn_prefill(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(seqlens), _ptr(o), _ptr(lse), B, H, Hkv, Tq, D, Tmax,
+                                int(window), float(scale), _stream(stream, q.device)),
+           "swattn_prefill")
+
+
 # ----------------------------------------------------------------------------- allocating wrappers
 def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
@@ -321,6 +344,17 @@ def bwd(q, k, v, o, do, lse, window: int = -1, scale: float | None = None, strea
     else:
         swattn_bwd(q, k, v, o, do, lse, dq, dk, dv, window, scale, workspace, stream)
     return dq, dk, dv
+
+
+def prefill(q, k_new, v_new, k_cache, v_cache, seqlens, window: int = -1,
+            scale: float | None = None, stream=None, with_lse: bool = True):
+    """Appends the chunk to the caches in place and returns (o, lse) of its queries."""
+    B, Tq, H, D = q.shape
+    scale = default_scale(D) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device) if with_lse else None
+    swattn_prefill(q, k_new, v_new, k_cache, v_cache, seqlens, o, lse, window, scale, stream)
+    return o, lse
 
 
 def decode(q, k_cache, v_cache, seqlens, window: int = -1, scale: float | None = None,

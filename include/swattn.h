@@ -166,6 +166,21 @@ int swattn_bwd_dq_f32(const float *q, const float *k, const float *v, const floa
                       int H, int T, int D, int window, float scale, swattn_stream_t stream);
 
 /*
+ * Chunked prefill with cache append (bf16; guide section 6: the engine fills the KV
+ * cache through the kernels' with-KV-cache entry).  q, o [B,Tq,H,D]; k_new, v_new
+ * [B,Tq,Hkv,D]; k_cache, v_cache [B,Tmax,Hkv,D]; seqlens device int32 [B], the rows
+ * already cached.  For sequence b, with L0 = seqlens[b] clamped to [0, Tmax - Tq],
+ * rows L0 .. L0+Tq-1 of the caches are overwritten with k_new[b], v_new[b], then query
+ * i attends as position L0 + i to cache rows j <= L0 + i inside the window (o and,
+ * unless NULL, lse [B,H,Tq]).  seqlens is not updated (the caller adds Tq).  Hkv = H
+ * without grouping.  INVALID_ARG also for Tmax <= 0 or Tq > Tmax.  No workspace.
+ */
+int swattn_prefill(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                   void *v_cache, const int *seqlens, void *o, float *lse, int B, int H,
+                   int Hkv, int Tq, int D, int Tmax, int window, float scale,
+                   swattn_stream_t stream);
+
+/*
  * Decode workspace in bytes: per (sequence, head, KV split) one float32 partial
  * output [D] and one partial LSE.  Depends on Tmax and window because they bound
  * the number of splits.  Returns 0 for invalid sizes.  No initialisation needed;

@@ -1,0 +1,123 @@
+"""GPU parity of chunked prefill with cache append (swattn_prefill) against the oracle.
+
+The chunk's K/V rows are written into the caches at seqlens[b] (clamped to
+[0, Tmax - Tq]) and its queries attend, as positions seqlens[b] + i, to the cache.
+Bars: bf16 max-abs <= 2e-2 and relative L2 <= 5e-3 on o, max-abs <= 1e-3 on lse;
+the written cache rows are bitwise the chunk's rows and no other cache row changes.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from causal_sliding_window_amd import inputs, swattn
+from oracle import attention as orc
+from parity import check
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _case(B, Tq, H, Hkv, D, Tmax, seqlens, seed):
+    x = inputs.training_inputs(B, Tq, H, D, "bf16", seed=seed, qk_norm=True, Hkv=Hkv)
+    c = inputs.decode_inputs(B, H, D, Tmax, "bf16", seed=seed + 50, lengths=seqlens, Hkv=Hkv)
+    return {"q": x["q"], "k_new": x["k"], "v_new": x["v"], "k_cache": c["k_cache"],
+            "v_cache": c["v_cache"], "seqlens": c["seqlens"]}
+
+
+def _run(x, window, scale):
+    g = {n: t.to(DEV) for n, t in x.items()}
+    o, lse = swattn.prefill(g["q"], g["k_new"], g["v_new"], g["k_cache"], g["v_cache"],
+                            g["seqlens"], window, scale)
+    torch.cuda.synchronize()
+    return o, lse, g["k_cache"], g["v_cache"]
+
+
+def _oracle(x, window, scale):
+    f = inputs.to_f64
+    return orc.attn_prefill(f(x["q"]), f(x["k_new"]), f(x["v_new"]), f(x["k_cache"]),
+                            f(x["v_cache"]), x["seqlens"].numpy(), window, scale)
+
+
+@pytest.mark.parametrize("H,Hkv", [(6, 6), (6, 2)])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("W", [-1, 1, 65, 300])
+def test_prefill_vs_oracle(H, Hkv, D, W):
+    """Offsets on and off the 32-row tile grid (0, 37, 64, 300), a ragged chunk of 129
+    rows, and one length past Tmax - Tq (clamped)."""
+    lens = [0, 37, 64, 300, 900]
+    x = _case(len(lens), 129, H, Hkv, D, 700, lens, seed=H + Hkv + D + W)
+    scale = 1 / math.sqrt(D)
+    o, lse, kc, vc = _run(x, W, scale)
+    ro, rl, rkc, rvc = _oracle(x, W, scale)
+    check("o", o, ro, torch.bfloat16)
+    check("lse", lse, rl, torch.bfloat16, lse=True)
+    # the caches: the written rows are the chunk's bf16 rows, every other row unchanged
+    assert np.array_equal(inputs.to_f64(kc), rkc) and np.array_equal(inputs.to_f64(vc), rvc)
+
+
+def test_prefill_in_chunks_is_the_forward_of_the_whole():
+    """Three chunks (200, 77, 235 rows) from an empty cache give, row for row, the
+    forward over the whole 512-row sequence (compared with the oracle's forward)."""
+    B, H, Hkv, D, Tmax, W = 2, 4, 2, 128, 640, 150
+    x = inputs.training_inputs(B, 512, H, D, "bf16", seed=21, qk_norm=True, Hkv=Hkv)
+    g = {n: t.to(DEV) for n, t in x.items()}
+    kc = torch.zeros(B, Tmax, Hkv, D, dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    scale = 1 / math.sqrt(D)
+    outs, lses, start = [], [], 0
+    for n in (200, 77, 235):
+        seq = torch.full((B,), start, dtype=torch.int32, device=DEV)
+        sl = slice(start, start + n)
+        o, lse = swattn.prefill(g["q"][:, sl].contiguous(), g["k"][:, sl].contiguous(),
+                                g["v"][:, sl].contiguous(), kc, vc, seq, W, scale)
+        outs.append(o)
+        lses.append(lse)
+        start += n
+    torch.cuda.synchronize()
+    a = {n: inputs.to_f64(t) for n, t in x.items()}
+    ro, rl = orc.attn_fwd(a["q"], a["k"], a["v"], W, scale)
+    check("o", torch.cat(outs, dim=1), ro, torch.bfloat16)
+    check("lse", torch.cat(lses, dim=2), rl, torch.bfloat16, lse=True)
+
+
+def test_prefill_last_row_matches_decode():
+    """After a prefill, decode of the chunk's last query (seqlens + Tq rows) agrees with
+    the prefill's last row."""
+    lens = [5, 1000, 2047]
+    x = _case(3, 64, 8, 2, 128, 3000, lens, seed=31)
+    scale = 1 / math.sqrt(128)
+    o, lse, kc, vc = _run(x, 512, scale)
+    seq = (x["seqlens"] + 64).to(DEV)
+    od, ld = swattn.decode(x["q"][:, -1].contiguous().to(DEV), kc, vc, seq, 512, scale)
+    torch.cuda.synchronize()
+    assert torch.allclose(od.float(), o[:, -1].float(), atol=2e-2)
+    assert torch.allclose(ld, lse[:, :, -1], atol=1e-3)
+
+
+def test_prefill_full_size_sampled():
+    """Chunks of 512 queries for the decode workload's 32 sequences (H12 D128, cache of
+    4096 rows, each sequence's length from the decode generator minus 512): compared on
+    sampled sequences."""
+    c = inputs.CONFIGS["decode"]
+    B, H, D, Tmax, Tq = c["B"], c["H"], c["D"], c["Tmax"], 512
+    lens = np.maximum(inputs.decode_lengths(B, c["len_seed"], c["len_lo"], c["len_hi"]) - Tq, 0)
+    x = _case(B, Tq, H, H, D, Tmax, lens, seed=41)
+    scale = 1 / math.sqrt(D)
+    o, lse, kc, vc = _run(x, -1, scale)
+    pick = [0, 17, B - 1]
+    sub = {n: t[pick] for n, t in x.items()}
+    ro, rl, rkc, _ = _oracle(sub, -1, scale)
+    check("o", o[pick], ro, torch.bfloat16)
+    check("lse", lse[pick], rl, torch.bfloat16, lse=True)
+    assert np.array_equal(inputs.to_f64(kc[pick]), rkc)
+
+
+def test_prefill_rejects_bad_sizes():
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16, device=DEV)
+    kc = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16, device=DEV)  # Tmax 4 < Tq 8
+    seq = torch.zeros(1, dtype=torch.int32, device=DEV)
+    with pytest.raises(swattn.SwattnError):
+        swattn.prefill(q, q, q, kc, kc.clone(), seq)
