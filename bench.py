@@ -472,9 +472,11 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
 
     copy_f = copy_reading(fetch_csv, "FETCH_SIZE")
     copy_w = copy_reading(write_csv, "WRITE_SIZE")
-    names = {"fwd": "fwd_bf16_kernel",
-             "bwd_dkdv": "bwd_dkdv_bf16_kernel", "bwd_dq": "bwd_dq_bf16_kernel",
-             "decode_split": "decode_split_kernel"}
+    # the training and decode kernels of the small and decode workloads (not the grouped
+    # or prefill instantiations, which the same run also launches)
+    names = {"fwd": "fwd_bf16_kernel<128, false>",
+             "bwd_dkdv": "bwd_dkdv_bf16_kernel<128, false>", "bwd_dq": "bwd_dq_bf16_kernel<128>",
+             "decode_split": "decode_split_kernel<unsigned short, 128, false>"}
     out = {"source_hash": source_hash(), "copy_bytes": copy_bytes,
            "fetch_factor": copy_bytes / copy_f if copy_f else 1.0,
            "write_factor": copy_bytes / copy_w if copy_w else 1.0, "kernels": {}}
