@@ -237,9 +237,12 @@ __device__ __forceinline__ void dt_read_tr_perm_block(const uint16_t *tile, int 
 
 // Asynchronous 16-byte copy global -> LDS: lane l's 16 bytes land at lds + 16 l
 // (lds must be the same for the whole wave).  Completion is awaited with
-// s_waitcnt vmcnt before the barrier that publishes the tile.
+// s_waitcnt vmcnt before the barrier that publishes the tile.  CPOL: cache policy
+// bits of the load (2 = non-temporal, for data read exactly once).
+template <int CPOL = 0>
 __device__ __forceinline__ void copy16_to_lds(const void *src, void *lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0,
+                                   CPOL);
 }
 
 // Copy of 16 rows of one 32-column block of a row-major bf16 matrix (row stride
@@ -247,7 +250,7 @@ __device__ __forceinline__ void copy16_to_lds(const void *src, void *lds) {
 // rows: tile rows row16 .. row16+15 of block db.  With perm, tile row r of each
 // 32-row block is placed at LDS row swap23(r) (see dt_read_tr_perm).  One call per
 // wave moves 1 KB.
-template <int R>
+template <int R, int CPOL = 0>
 __device__ __forceinline__ void copy_rows16(uint16_t *tile, const uint16_t *src, int rs,
                                             int row_base, int nrows, int row16, int db,
                                             bool perm, int lane) {
@@ -255,7 +258,8 @@ __device__ __forceinline__ void copy_rows16(uint16_t *tile, const uint16_t *src,
   const int lc = (lane & 3) ^ ((r >> 2) & 3);        // logical chunk stored at this position
   const int trow = perm ? ((r & ~31) | swap23(r & 31)) : r;
   const int grow = min(row_base + trow, nrows - 1);
-  copy16_to_lds(src + (size_t)grow * rs + 32 * db + 8 * lc, tile + db * (R * 32) + row16 * 32);
+  copy16_to_lds<CPOL>(src + (size_t)grow * rs + 32 * db + 8 * lc,
+                      tile + db * (R * 32) + row16 * 32);
 }
 
 // Buffer resource over `nbytes` bytes from `base` (raw addressing, no stride):

@@ -11,11 +11,16 @@
 //   K/V row of one head is 256 contiguous bytes (bf16, D = 128) read by D/8 lanes
 //   with non-temporal 16-byte loads; every wave requests all of its rows before
 //   using any.
+// decode_gqa_mfma_kernel: the same split for bf16, D = 128 and groups of at least
+//   kGqaMfmaMinGroup query heads per K/V head, on the matrix cores (the group's heads
+//   are the columns of S^T = K Q^T and of O^T = V^T P); same workspace and partials.
 // decode_merge_kernel: lse = ln sum_c exp(lse_c), o = sum_c exp(lse_c - lse) o_c.
 //   A separate launch: merging inside the split kernel needs agent-scope fences,
 //   which on this chip write back and invalidate an XCD's whole L2 per workgroup.
 #include "common.h"
 #include "launch.h"
+
+#include <type_traits>
 
 namespace swattn {
 
@@ -324,6 +329,211 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   }
 }
 
+// Grouped decode on the matrix cores (bf16, D = 128): the G = H / Hkv query heads
+// that read K/V head hk form the 32 columns of one MFMA operand, so each cache row
+// costs a share of two 32 x 32 x 16 products instead of a vector-ALU dot product per
+// query head.  Workgroup (hk, chunk c, b), four waves; wave w holds rows 32w ..
+// 32w + 31 of the chunk's kDecodeChunk rows.
+//   1. S^T (rows x heads) = K Q^T: K rows straight from HBM into A operands (tile
+//      row swap23(m) in operand row m), q of up to 32 heads as B operands; V rows
+//      copied into an LDS tile meanwhile.
+//   2. Softmax in exp2 units against the chunk's maximum per head (wave maxima
+//      exchanged through LDS), P rounded to bf16 and written to LDS per head.
+//   3. O^T = V^T P: wave w forms the 32 columns 32w .. 32w + 31 of every head's
+//      output over all the chunk's rows (V^T by transposed LDS reads), divides by
+//      the row sum and writes the chunk's partial (o_c, lse_c) as the vector kernel.
+// More than 32 heads per group: batches of 32 in turn; K stays in registers and V
+// in LDS between batches.
+constexpr int kGqaHeads = 32;
+// Smallest group taken by the matrix-core kernel.  Measured on the 32-sequence
+// decode workload (H = 12): with 2 query heads per K/V head the vector-ALU kernel is
+// faster (its loads are fully coalesced and it holds no LDS tile); from 3 on the
+// matrix-core kernel is as fast or faster, 2x at 12.
+constexpr int kGqaMfmaMinGroup = 3;
+constexpr int kGqaPitch = kDecodeChunk + 8;  // P tile row pitch (bf16): rows land on distinct banks
+
+__global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ vc, const int *__restrict__ seqlens, float *__restrict__ ws_o,
+    float *__restrict__ ws_lse, uint16_t *__restrict__ o, float *__restrict__ lse, int H, int Hkv,
+    int Tmax, int window, float scale, int nsplit) {
+  constexpr int D = 128, NDB = D / 32, CH = kDecodeChunk;
+  static_assert(CH == 128 && NDB == 4, "one 32-row block per wave, one d block per wave");
+  __shared__ __attribute__((aligned(16))) uint16_t vt[NDB * CH * 32];  // V rows, d-block-major
+  __shared__ __attribute__((aligned(16))) uint16_t pt[kGqaHeads * kGqaPitch];  // P^T, per head
+  __shared__ float red_m[4][kGqaHeads], red_l[4][kGqaHeads];
+
+  const int hk = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+  const int G = H / Hkv;
+  const int L = min(seqlens[b], Tmax);
+  if (L <= 0) {  // empty sequence: o = 0, lse = -inf
+    if (c == 0) {
+      for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+        o[((size_t)b * H + hk * G) * D + i] = 0;
+      if (lse)
+        for (int g = threadIdx.x; g < G; g += blockDim.x) lse[b * H + hk * G + g] = -INFINITY;
+    }
+    return;
+  }
+  const int lo = visible_lo(L, window);
+  const int n = L - lo;
+  if (c * CH >= n) return;
+  const int t0 = lo + c * CH;
+  const int cnt = min(CH, L - t0);
+  const int nch = (n + CH - 1) / CH;
+
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, col = lane & 31;
+  const size_t rs = (size_t)Hkv * D;
+  const uint16_t *kb = kc + ((size_t)b * Tmax * Hkv + hk) * D;
+  const uint16_t *vb = vc + ((size_t)b * Tmax * Hkv + hk) * D;
+
+  // K: load (u, s) reads rows 32w + 16u + l/4 in 64-byte pieces (chunks 4s .. 4s + 3,
+  // columns 32s .. 32s + 31), rows past the chunk clamped to its last row.  A lane
+  // permute then gives lane l row 16u + l % 16 and chunk 4s + l / 16: the A operand
+  // of a 16 x 16 x 32 product (row = l % 16, 8 k values per lane).  Loading the
+  // operand directly would put four adjacent 16-byte pieces in four lanes 16 apart
+  // and cost the memory pipeline 64 separate requests per load.
+  bf16x8 ka[2][NDB];
+  {
+    u32x4 raw[2][NDB];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = min(32 * w + 16 * u + (lane >> 2), cnt - 1);
+      const uint16_t *kr = kb + (size_t)(t0 + r) * rs + 8 * (lane & 3);
+#pragma unroll
+      for (int s = 0; s < NDB; ++s) raw[u][s] = ldg16_stream(kr + 32 * s);
+    }
+    const int src = 4 * (4 * (lane & 15) + (lane >> 4));  // byte address of the source lane
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int s = 0; s < NDB; ++s) {
+        u32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __builtin_amdgcn_ds_bpermute(src, raw[u][s][e]);
+        ka[u][s] = __builtin_bit_cast(bf16x8, x);
+      }
+  }
+  // V: this wave's 32 rows into the tile, non-temporal (rows past the chunk clamped,
+  // never used)
+#pragma unroll
+  for (int r16 = 0; r16 < 2; ++r16)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      copy_rows16<CH, 2>(vt, vb, (int)rs, t0, t0 + cnt, 32 * w + 16 * r16, db, false, lane);
+
+  const float qs = scale * kLog2e;  // scores in exp2 units
+  const int l16 = lane & 15, q4 = lane >> 4;
+  for (int g0 = 0; g0 < G; g0 += kGqaHeads) {
+    const int gn = min(kGqaHeads, G - g0);
+    const int ntile = (gn + 15) / 16;  // 16-head column tiles of S^T
+    const bool hv = col < gn;  // this lane's P V column is a query head of the batch
+    const size_t bh = (size_t)b * H + hk * G + g0 + col;
+    // S^T (rows x heads) in 16 x 16 tiles: tile (u, nt) register i of lane l holds
+    // row 32w + 16u + 4(l/16) + i of head 16nt + l % 16
+    f32x4 sacc[2][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      if (nt < ntile) {
+        const int hq = 16 * nt + l16;
+        bf16x8 qb[NDB];
+        const uint16_t *qr = q + ((size_t)b * H + hk * G + g0 + hq) * D + 8 * q4;
+#pragma unroll
+        for (int s = 0; s < NDB; ++s)
+          qb[s] = hq < gn ? __builtin_bit_cast(bf16x8, ldg16(qr + 32 * s)) : bf16x8{};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          f32x4 a = {};
+#pragma unroll
+          for (int s = 0; s < NDB; ++s)
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u][s], qb[s], a, 0, 0, 0);
+          sacc[u][nt] = a;
+        }
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      if (nt < ntile) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = 32 * w + 16 * u + 4 * q4 + i < cnt ? sacc[u][nt][i] * qs : -INFINITY;
+            sacc[u][nt][i] = x;
+            m = fmaxf(m, x);
+          }
+        m = xhalf_max(swap16_max(m));
+        if (q4 == 0) red_m[w][16 * nt + l16] = m;
+      }
+    }
+    __syncthreads();  // also completes this wave's V copies before the tile is read
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      if (nt < ntile) {
+        const int hq = 16 * nt + l16;
+        const float Mq =
+            fmaxf(fmaxf(red_m[0][hq], red_m[1][hq]), fmaxf(red_m[2][hq], red_m[3][hq]));
+        float l = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float p[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[i] = fast_exp2(sacc[u][nt][i] - Mq);  // rows past the chunk: exp2(-inf) = 0
+            l += p[i];
+          }
+          // four consecutive rows of head hq: one 8-byte write into its P^T row
+          u32x2 pk;
+          pk[0] = f32_to_bf16_bits(p[0]) | ((uint32_t)f32_to_bf16_bits(p[1]) << 16);
+          pk[1] = f32_to_bf16_bits(p[2]) | ((uint32_t)f32_to_bf16_bits(p[3]) << 16);
+          *reinterpret_cast<u32x2 *>(pt + hq * kGqaPitch + 32 * w + 16 * u + 4 * q4) = pk;
+        }
+        l = xhalf_sum(swap16_sum(l));
+        if (q4 == 0) red_l[w][hq] = l;
+      }
+    }
+    __syncthreads();
+
+    f32x16 oacc = {};
+#pragma unroll
+    for (int t = 0; t < CH / 16; ++t) {
+      const bf16x8 va = dt_read_tr<CH>(vt, 16 * t, w, lane);
+      const bf16x8 pb = lds_read_b128(pt + col * kGqaPitch + 16 * t + 8 * h);
+      oacc = mfma32(va, pb, oacc);
+    }
+    const float M = fmaxf(fmaxf(red_m[0][col], red_m[1][col]), fmaxf(red_m[2][col], red_m[3][col]));
+    const float Ltot = red_l[0][col] + red_l[1][col] + red_l[2][col] + red_l[3][col];
+    if (hv) {
+      const float inv = 1.f / Ltot;
+      const size_t slot = bh * nsplit + c;
+      // register i holds output column 32w + 8(i/4) + 4h + i%4 of head col
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 32 * w + 8 * e + 4 * h;
+        if (nch == 1) {
+          u32x2 pk;
+          pk[0] = f32_to_bf16_bits(oacc[4 * e] * inv) |
+                  ((uint32_t)f32_to_bf16_bits(oacc[4 * e + 1] * inv) << 16);
+          pk[1] = f32_to_bf16_bits(oacc[4 * e + 2] * inv) |
+                  ((uint32_t)f32_to_bf16_bits(oacc[4 * e + 3] * inv) << 16);
+          *reinterpret_cast<u32x2 *>(o + bh * D + d) = pk;
+        } else {
+          f32x4 v4 = {oacc[4 * e] * inv, oacc[4 * e + 1] * inv, oacc[4 * e + 2] * inv,
+                      oacc[4 * e + 3] * inv};
+          *reinterpret_cast<f32x4 *>(ws_o + slot * D + d) = v4;
+        }
+      }
+      if (w == 0 && h == 0) {
+        const float lv = M * kLn2 + logf(Ltot);
+        if (nch > 1) ws_lse[slot] = lv;
+        else if (lse) lse[bh] = lv;
+      }
+    }
+    if (g0 + kGqaHeads < G) __syncthreads();  // red_m, red_l and pt are written again
+  }
+}
+
 template <typename TT, int D>
 static hipError_t launch_decode_t(const void *q, const void *k_cache, const void *v_cache,
                                   const int *seqlens, void *o, float *lse, int B, int H,
@@ -332,7 +542,11 @@ static hipError_t launch_decode_t(const void *q, const void *k_cache, const void
   const int ns = decode_num_splits(Tmax, window);
   float *ws_o = ws;
   float *ws_lse = ws + (size_t)B * H * ns * D;
-  if (Hkv != H)
+  if (std::is_same<TT, uint16_t>::value && D == 128 && H >= kGqaMfmaMinGroup * Hkv)
+    decode_gqa_mfma_kernel<<<dim3(Hkv, ns, B), 256, 0, st>>>(
+        (const uint16_t *)q, (const uint16_t *)k_cache, (const uint16_t *)v_cache, seqlens, ws_o,
+        ws_lse, (uint16_t *)o, lse, H, Hkv, Tmax, window, scale, ns);
+  else if (Hkv != H)
     decode_split_kernel<TT, D, true><<<dim3(Hkv, ns, B), 256, 0, st>>>(
         (const TT *)q, (const TT *)k_cache, (const TT *)v_cache, seqlens, ws_o, ws_lse, (TT *)o,
         lse, H, Hkv, Tmax, window, scale, ns);

@@ -119,10 +119,13 @@ def _decode_oracle(d, W, scale):
     return orc.attn_decode(a["q"], a["k_cache"], a["v_cache"], d["seqlens"].numpy(), W, scale)
 
 
-@pytest.mark.parametrize("H,Hkv", [(8, 1), (8, 2), (8, 4), (12, 3)])
+@pytest.mark.parametrize("H,Hkv", [(8, 1), (8, 2), (8, 4), (12, 3), (64, 2), (40, 1)])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("W", [-1, 100])
 def test_gqa_decode_vs_oracle(H, Hkv, D, W):
+    """Groups of 2 to 40 query heads (the bf16 D = 128 kernel takes them 32 at a time:
+    40 needs two batches, 32 fills one); lengths of 0, 1, one row past a chunk, and
+    ragged chunk tails."""
     lens = [0, 1, 129, 700, 1000, 257]
     d = inputs.decode_inputs(len(lens), H, D, 1000, "bf16", seed=H + Hkv + D, lengths=lens,
                              Hkv=Hkv)
@@ -137,10 +140,14 @@ def test_gqa_decode_vs_oracle(H, Hkv, D, W):
     check("lse", lse[1:], rl[1:], torch.bfloat16, lse=True)
 
 
-def test_gqa_decode_equals_ungrouped_on_repeated_cache():
+@pytest.mark.parametrize("D", [64, 128])
+def test_gqa_decode_equals_ungrouped_on_repeated_cache(D):
     """Grouped decode reads each cache row once for its group; with the cache repeated
-    over the group, the ungrouped decode gives bitwise the same o and lse."""
-    B, H, Hkv, D, Tmax = 6, 12, 4, 128, 3000
+    over the group, the ungrouped decode computes the same thing.  D = 64 runs the
+    same vector-ALU arithmetic on both paths (bitwise equal); D = 128 bf16 runs the
+    grouped matrix-core kernel, which rounds P to bf16 before P V as the forward does,
+    so the two agree to the bf16 bar (both also against the oracle)."""
+    B, H, Hkv, Tmax = 6, 12, 4, 3000
     d = inputs.decode_inputs(B, H, D, Tmax, "bf16", seed=9, Hkv=Hkv)
     g = _gpu(d)
     G = H // Hkv
@@ -150,7 +157,15 @@ def test_gqa_decode_equals_ungrouped_on_repeated_cache():
         o, lse = swattn.decode(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], W)
         o2, lse2 = swattn.decode(g["q"], kc, vc, g["seqlens"], W)
         torch.cuda.synchronize()
-        assert torch.equal(o, o2) and torch.equal(lse, lse2), W
+        if D == 64:
+            assert torch.equal(o, o2) and torch.equal(lse, lse2), W
+        else:
+            ro, rl = _decode_oracle(d, W, 1 / math.sqrt(D))
+            for got in (o, o2):
+                check("o", got, ro, torch.bfloat16)
+            for got in (lse, lse2):
+                check("lse", got, rl, torch.bfloat16, lse=True)
+            check("o vs ungrouped", o, f64(o2), torch.bfloat16)
 
 
 def test_gqa_decode_long_cache_mqa():
