@@ -242,6 +242,43 @@ def bench_decode(torch, swattn, inputs, iters, hkv=None):
     return out
 
 
+def bench_prologue(torch, swattn, inputs, iters, cfg_name="small"):
+    """QK-norm + rotary prologue on a training workload's raw q and k (one launch for
+    both), forward and backward, cold (a 1 GiB fill before each call).  Bytes: the
+    forward reads q, k and writes q', k'; the backward reads q, k, dq', dk' and writes
+    dq, dk."""
+    c = inputs.CONFIGS[cfg_name]
+    B, T, H, D = c["B"], c["T"], c["H"], c["D"]
+    x = inputs.training_inputs(B, T, H, D, c["dtype"], c["seeds"][0], qk_norm=False)
+    q, k, dy = (x[n].to("cuda:0") for n in ("q", "k", "do"))
+    yq, yk = torch.empty_like(q), torch.empty_like(k)
+    dq, dk = torch.empty_like(q), torch.empty_like(k)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+    calls = {"forward": lambda: swattn.swattn_qk_norm_rope(q, k, yq, yk),
+             "backward": lambda: swattn.swattn_qk_norm_rope_bwd(q, k, dy, dy, dq, dk)}
+    tensor_bytes = q.numel() * q.element_size()
+    res = {"workload": f"{cfg_name}: q and k [{B},{T},{H},{D}] bf16, raw"}
+    for name, call in calls.items():
+        for _ in range(3):
+            call()
+        ts = []
+        for _ in range(iters):
+            flush.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        nb = (4 if name == "forward" else 6) * tensor_bytes
+        ms = statistics.median(ts)
+        res[name] = {"bytes": nb, "us_cold_median": round(ms * 1e3, 2),
+                     "GB_per_s": round(nb / (ms * 1e-3) / 1e9, 1),
+                     "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del flush
+    return res
+
+
 def bench_prefill(torch, swattn, inputs, iters, tq=512):
     """Chunked prefill on the decode workload's caches: each of the 32 sequences appends a
     chunk of ``tq`` tokens at (its decode length - tq) and attends the chunk's queries to
@@ -593,6 +630,8 @@ def main():
         log(f"decode gqa {res['decode_gqa']}")
         res["prefill"] = bench_prefill(torch, swattn, inputs, args.decode_iters)
         log(f"prefill {res['prefill']}")
+        res["qk_prologue"] = bench_prologue(torch, swattn, inputs, args.decode_iters)
+        log(f"qk prologue {res['qk_prologue']}")
     if args.hkv:
         res["training_gqa"] = bench_training_gqa(torch, swattn, inputs, args.config, args.hkv,
                                                  max(50, args.steps // 4), max(50, args.warmup // 2))

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libswattn.so")
-SOURCES = ["api.hip", "fwd_bf16.hip", "bwd_bf16.hip", "dkdv_bf16.hip", "decode.hip", "f32.hip"]
+SOURCES = ["api.hip", "fwd_bf16.hip", "bwd_bf16.hip", "dkdv_bf16.hip", "decode.hip", "f32.hip",
+           "prologue.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -2,6 +2,8 @@
 // Validates arguments, sizes workspaces and enqueues the kernels on the caller's
 // stream.  No allocation, no host synchronisation, no global state.
 #include <limits.h>
+
+#include <cmath>
 #include <initializer_list>
 #include <stdint.h>
 
@@ -10,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 102;  // 0.1.2: grouped-query entry points (*_gqa)
+constexpr int kVersion = 103;  // 0.1.3: QK-norm + rotary prologue (swattn_qk_norm_rope*)
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -320,6 +322,37 @@ int swattn_decode_f32(const float *q, const float *k_cache, const float *v_cache
                       int window, float scale, void *workspace, swattn_stream_t stream) {
   return decode_common(false, q, k_cache, v_cache, seqlens, o, lse, B, H, H, D, Tmax, window,
                        scale, workspace, stream);
+}
+
+static int check_prologue(int B, int T, int H, int Hkv, int D, float base, float eps) {
+  if (B <= 0 || T <= 0 || H <= 0 || Hkv <= 0 || D <= 0) return SWATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return SWATTN_ERR_UNSUPPORTED;
+  if (!(base > 0.f) || !std::isfinite(base) || !(eps >= 0.f) || !std::isfinite(eps))
+    return SWATTN_ERR_INVALID_ARG;
+  if ((long long)B * T > INT_MAX / 2) return SWATTN_ERR_INVALID_ARG;  // 32-bit row indices
+  return SWATTN_OK;
+}
+
+int swattn_qk_norm_rope(const void *q, const void *k, void *q_out, void *k_out,
+                        const int *pos_offset, int B, int T, int H, int Hkv, int D, float base,
+                        float eps, swattn_stream_t stream) {
+  const int st = check_prologue(B, T, H, Hkv, D, base, eps);
+  if (st != SWATTN_OK) return st;
+  if (!all_aligned({q, k, q_out, k_out})) return SWATTN_ERR_INVALID_ARG;
+  return hip_status(swattn::launch_qk_norm_rope(q, k, q_out, k_out, pos_offset, B, T, H, Hkv, D,
+                                                base, eps, (hipStream_t)stream));
+}
+
+int swattn_qk_norm_rope_bwd(const void *q, const void *k, const void *dq_out,
+                            const void *dk_out, void *dq, void *dk, const int *pos_offset, int B,
+                            int T, int H, int Hkv, int D, float base, float eps,
+                            swattn_stream_t stream) {
+  const int st = check_prologue(B, T, H, Hkv, D, base, eps);
+  if (st != SWATTN_OK) return st;
+  if (!all_aligned({q, k, dq_out, dk_out, dq, dk})) return SWATTN_ERR_INVALID_ARG;
+  return hip_status(swattn::launch_qk_norm_rope_bwd(q, k, dq_out, dk_out, dq, dk, pos_offset, B,
+                                                    T, H, Hkv, D, base, eps,
+                                                    (hipStream_t)stream));
 }
 
 }  // extern "C"

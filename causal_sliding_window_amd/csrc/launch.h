@@ -64,4 +64,14 @@ hipError_t launch_decode(bool bf16, const void *q, const void *k_cache, const vo
                          const int *seqlens, void *o, float *lse, int B, int H, int Hkv, int D,
                          int Tmax, int window, float scale, float *ws, hipStream_t st);
 
+// QK-norm + rotary prologue (prologue.hip): q, k -> q_out, k_out; and its backward
+// (dq_out, dk_out, with the raw q, k -> dq, dk).  pos_off: device int32[B] or null.
+hipError_t launch_qk_norm_rope(const void *q, const void *k, void *q_out, void *k_out,
+                               const int *pos_off, int B, int T, int H, int Hkv, int D,
+                               float base, float eps, hipStream_t st);
+hipError_t launch_qk_norm_rope_bwd(const void *q, const void *k, const void *dq_out,
+                                   const void *dk_out, void *dq, void *dk, const int *pos_off,
+                                   int B, int T, int H, int Hkv, int D, float base, float eps,
+                                   hipStream_t st);
+
 }  // namespace swattn

@@ -50,6 +50,8 @@ _SIGS = {
     "swattn_bwd_gqa": ([_P] * 9 + [_I] * 6 + [_F, _P, _P], _I),
     "swattn_decode_gqa": ([_P] * 6 + [_I] * 6 + [_F, _P, _P], _I),
     "swattn_prefill": ([_P] * 8 + [_I] * 7 + [_F, _P], _I),
+    "swattn_qk_norm_rope": ([_P] * 5 + [_I] * 5 + [_F, _F, _P], _I),
+    "swattn_qk_norm_rope_bwd": ([_P] * 7 + [_I] * 5 + [_F, _F, _P], _I),
 }
 
 
@@ -313,6 +315,39 @@ def swattn_prefill(q, k_new, v_new, k_cache, v_cache, seqlens, o, lse, window: i
            "swattn_prefill")
 
 
+def _prologue_shapes(q, k, pos_offset, tensors):
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    for n, t in tensors:
+        _dev_tensor(t, n, torch.bfloat16, (B, T, H, D) if n.startswith(("q", "dq")) else
+                    (B, T, Hkv, D))
+    if pos_offset is not None:
+        _dev_tensor(pos_offset, "pos_offset", torch.int32, (B,))
+    return B, T, H, Hkv, D
+
+
+def swattn_qk_norm_rope(q, k, q_out, k_out, pos_offset=None, base: float = 10000.0,
+                        eps: float = 1e-6, stream=None):
+    """QK-norm + rotary prologue (bf16): q [B,T,H,D], k [B,T,Hkv,D] -> q_out, k_out;
+    token t of sequence b at position max(pos_offset[b], 0) + t (t without offsets)."""
+    B, T, H, Hkv, D = _prologue_shapes(q, k, pos_offset, (("q", q), ("k", k), ("q_out", q_out),
+                                                          ("k_out", k_out)))
+    _check(lib().swattn_qk_norm_rope(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(pos_offset),
+                                     B, T, H, Hkv, D, float(base), float(eps),
+                                     _stream(stream, q.device)), "swattn_qk_norm_rope")
+
+
+def swattn_qk_norm_rope_bwd(q, k, dq_out, dk_out, dq, dk, pos_offset=None,
+                            base: float = 10000.0, eps: float = 1e-6, stream=None):
+    """Backward of the prologue: raw q, k and the gradients of its outputs -> dq, dk."""
+    B, T, H, Hkv, D = _prologue_shapes(q, k, pos_offset, (
+        ("q", q), ("k", k), ("dq_out", dq_out), ("dk_out", dk_out), ("dq", dq), ("dk", dk)))
+    _check(lib().swattn_qk_norm_rope_bwd(_ptr(q), _ptr(k), _ptr(dq_out), _ptr(dk_out), _ptr(dq),
+                                         _ptr(dk), _ptr(pos_offset), B, T, H, Hkv, D, float(base),
+                                         float(eps), _stream(stream, q.device)),
+           "swattn_qk_norm_rope_bwd")
+
+
 # ----------------------------------------------------------------------------- allocating wrappers
 def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
@@ -372,3 +407,18 @@ def decode(q, k_cache, v_cache, seqlens, window: int = -1, scale: float | None =
     else:
         swattn_decode(q, k_cache, v_cache, seqlens, o, lse, window, scale, workspace, stream)
     return o, lse
+
+
+def qk_norm_rope(q, k, pos_offset=None, base: float = 10000.0, eps: float = 1e-6, stream=None):
+    """Returns (q', k'): every head vector RMS-normalised and rotated by its position."""
+    q_out, k_out = torch.empty_like(q), torch.empty_like(k)
+    swattn_qk_norm_rope(q, k, q_out, k_out, pos_offset, base, eps, stream)
+    return q_out, k_out
+
+
+def qk_norm_rope_bwd(q, k, dq_out, dk_out, pos_offset=None, base: float = 10000.0,
+                     eps: float = 1e-6, stream=None):
+    """Returns (dq, dk) for the raw q, k given the gradients of (q', k')."""
+    dq, dk = torch.empty_like(q), torch.empty_like(k)
+    swattn_qk_norm_rope_bwd(q, k, dq_out, dk_out, dq, dk, pos_offset, base, eps, stream)
+    return dq, dk

@@ -215,6 +215,39 @@ int swattn_decode_gqa(const void *q, const void *k_cache, const void *v_cache,
                       int D, int Tmax, int window, float scale, void *workspace,
                       swattn_stream_t stream);
 
+/*
+ * QK-norm + rotary prologue (bf16; nanochat release article, architecture list:
+ * rotary embeddings as the only position encoding, QK norm, RMSNorm without
+ * learnable parameters; guide section 1 "GPT model", feature list).  For every
+ * head vector x [D] of q [B,T,H,D] and k [B,T,Hkv,D], token t of sequence b at
+ * position p = max(pos_offset[b], 0) + t (p = t when pos_offset is NULL; device
+ * int32 [B] otherwise):
+ *   x_n = x / sqrt(mean(x^2) + eps), no weight;
+ *   pair i = (x_n[i], x_n[i + D/2]), i < D/2, rotated by the angle p * base^(-2i/D):
+ *   y[i] = a cos - b sin, y[i + D/2] = a sin + b cos   (a, b the pair).
+ * Writes y into q_out [B,T,H,D] and k_out [B,T,Hkv,D] (bf16, rounded to nearest
+ * even from fp32; angles in fp64).  Hkv is independent of H here (any >= 1).
+ * Outputs may be their own inputs (in place); other overlaps are not allowed.
+ * INVALID_ARG: a NULL or misaligned tensor, B, T, H, Hkv <= 0, base <= 0, eps < 0
+ * or either not finite, B * T > INT_MAX / 2.  UNSUPPORTED: D not 64 or 128.
+ * Asynchronous on `stream`; no workspace.
+ */
+int swattn_qk_norm_rope(const void *q, const void *k, void *q_out, void *k_out,
+                        const int *pos_offset, int B, int T, int H, int Hkv, int D, float base,
+                        float eps, swattn_stream_t stream);
+
+/*
+ * Backward of swattn_qk_norm_rope: given the raw inputs q, k and the gradients of
+ * its outputs dq_out [B,T,H,D], dk_out [B,T,Hkv,D], writes dq, dk (same shapes,
+ * bf16): with g = dy rotated back by -angle and r = 1 / sqrt(mean(x^2) + eps),
+ * dx = r g - r^3 x (x . g) / D.  Same positions, arguments and errors as the
+ * forward; dq may be dq_out and dk may be dk_out (in place).
+ */
+int swattn_qk_norm_rope_bwd(const void *q, const void *k, const void *dq_out,
+                            const void *dk_out, void *dq, void *dk, const int *pos_offset, int B,
+                            int T, int H, int Hkv, int D, float base, float eps,
+                            swattn_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -122,6 +122,23 @@ def test_gqa_argument_errors():
     assert lib.swattn_decode_gqa(*p6, 1, 6, 2, 80, 16, -1, 1.0, FAKE, None) == 2
 
 
+def test_prologue_argument_errors():
+    """QK-norm + rotary prologue: sizes, D, base and eps are checked before any launch."""
+    lib = swattn.lib()
+    p4, p6 = [FAKE] * 4, [FAKE] * 6
+    # q, k, q_out, k_out, pos_offset, B, T, H, Hkv, D, base, eps, stream
+    assert lib.swattn_qk_norm_rope(*p4, None, 1, 8, 6, 0, 64, 1e4, 1e-6, None) == 1
+    assert lib.swattn_qk_norm_rope(*p4, None, 0, 8, 6, 2, 64, 1e4, 1e-6, None) == 1
+    assert lib.swattn_qk_norm_rope(*p4, None, 1, 8, 6, 2, 96, 1e4, 1e-6, None) == 2
+    assert lib.swattn_qk_norm_rope(*p4, None, 1, 8, 6, 2, 64, 0.0, 1e-6, None) == 1
+    assert lib.swattn_qk_norm_rope(*p4, None, 1, 8, 6, 2, 64, 1e4, -1.0, None) == 1
+    assert lib.swattn_qk_norm_rope(*p4, None, 1, 8, 6, 2, 64, float("nan"), 1e-6, None) == 1
+    assert lib.swattn_qk_norm_rope(None, FAKE, FAKE, FAKE, None, 1, 8, 6, 2, 64, 1e4, 1e-6,
+                                   None) == 1
+    assert lib.swattn_qk_norm_rope_bwd(*p6, None, 1, 8, 6, 2, 128, 1e4, float("inf"), None) == 1
+    assert lib.swattn_qk_norm_rope_bwd(*p6, None, 1, 0, 6, 2, 128, 1e4, 1e-6, None) == 1
+
+
 def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(swattn.SwattnError):
