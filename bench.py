@@ -250,12 +250,13 @@ def bench_prologue(torch, swattn, inputs, iters, cfg_name="small"):
     c = inputs.CONFIGS[cfg_name]
     B, T, H, D = c["B"], c["T"], c["H"], c["D"]
     x = inputs.training_inputs(B, T, H, D, c["dtype"], c["seeds"][0], qk_norm=False)
-    q, k, dy = (x[n].to("cuda:0") for n in ("q", "k", "do"))
+    # distinct gradient buffers for q' and k' (dO and v of the workload serve)
+    q, k, dyq, dyk = (x[n].to("cuda:0") for n in ("q", "k", "do", "v"))
     yq, yk = torch.empty_like(q), torch.empty_like(k)
     dq, dk = torch.empty_like(q), torch.empty_like(k)
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
     calls = {"forward": lambda: swattn.swattn_qk_norm_rope(q, k, yq, yk),
-             "backward": lambda: swattn.swattn_qk_norm_rope_bwd(q, k, dy, dy, dq, dk)}
+             "backward": lambda: swattn.swattn_qk_norm_rope_bwd(q, k, dyq, dyk, dq, dk)}
     tensor_bytes = q.numel() * q.element_size()
     res = {"workload": f"{cfg_name}: q and k [{B},{T},{H},{D}] bf16, raw"}
     for name, call in calls.items():
