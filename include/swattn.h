@@ -209,7 +209,10 @@ int swattn_decode_f32(const float *q, const float *k_cache,
 /* Grouped-query decode (bf16): k_cache, v_cache [B,Tmax,Hkv,D]; each cache row is
  * read once for the H / Hkv query heads of its group.  The workspace is
  * swattn_decode_workspace_size(B, H, D, Tmax, window) bytes (partials per query
- * head); otherwise as swattn_decode. */
+ * head); otherwise as swattn_decode.  With D = 128 and groups of 3 or more query
+ * heads the scores and P V run on the matrix cores, with P rounded to bf16 before
+ * P V as in the forward: results then differ from the ungrouped call on repeated
+ * caches by rounding only (still deterministic). */
 int swattn_decode_gqa(const void *q, const void *k_cache, const void *v_cache,
                       const int *seqlens, void *o, float *lse, int B, int H, int Hkv,
                       int D, int Tmax, int window, float scale, void *workspace,
