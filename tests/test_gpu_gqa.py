@@ -168,6 +168,23 @@ def test_gqa_decode_equals_ungrouped_on_repeated_cache(D):
             check("o vs ungrouped", o, f64(o2), torch.bfloat16)
 
 
+@pytest.mark.parametrize("H,Hkv", [(12, 4), (16, 1), (33, 1)])
+@pytest.mark.parametrize("W", [-1, 127, 128, 129, 5000])
+def test_gqa_decode_chunk_edges(H, Hkv, W):
+    """Lengths on and next to the 128-row chunk edges (127, 128, 129, 256, 384 + 1) and
+    windows either side of one chunk; groups of 3, 16 and 33 query heads (the last
+    with a one-head second batch on the matrix-core kernel)."""
+    lens = [127, 128, 129, 256, 385, 1024]
+    d = inputs.decode_inputs(len(lens), H, 128, 1024, "bf16", seed=H + W, lengths=lens, Hkv=Hkv)
+    g = _gpu(d)
+    scale = 1 / math.sqrt(128)
+    o, lse = swattn.decode(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], W, scale)
+    torch.cuda.synchronize()
+    ro, rl = _decode_oracle(d, W, scale)
+    check("o", o, ro, torch.bfloat16)
+    check("lse", lse, rl, torch.bfloat16, lse=True)
+
+
 def test_gqa_decode_long_cache_mqa():
     """One K/V head for all query heads (multi-query), 20000-row caches."""
     lens = [20000, 9001]
