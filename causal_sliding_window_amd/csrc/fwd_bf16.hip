@@ -25,7 +25,9 @@
 // The same kernel serves chunked prefill (PREFILL): T query rows of a sequence sit at
 // positions off .. off + T - 1 of a KV cache of Tkv rows, which already holds the
 // chunk's own K/V rows (cache_append_kernel runs first), with off = seqlens[b] read
-// on the device and clamped to [0, Tkv - T].  Band, masks and tiles work in absolute
+// on the device and clamped to [0, Tkv - T].  Work per (sequence, query tile) grows
+// with off, so the prefill grid takes its items longest first (sequences ranked by
+// off on the device).  Band, masks and tiles work in absolute
 // positions; q, o and lse are indexed within the chunk.  With off not a multiple of
 // 32 a wave's diagonal spans two key tiles, so every tile from the first one the
 // diagonal touches runs the element mask.
@@ -47,6 +49,10 @@ struct FwdCfg {
   static constexpr int CPW = TSZ * 2 / 1024 / 4;  // 1-KB copies per wave and tile
 };
 
+// Prefill: up to this many sequences, workgroups take (sequence, query tile) items
+// longest first, ranked on the device by cache offset.
+constexpr int kPrefillOrderMaxB = 256;
+
 // Row-max growth (exp2 units) tolerated before the running max is moved.
 constexpr float kRescaleLog2 = 8.f;
 
@@ -62,9 +68,35 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 
   const int BH = B * H;
   const int bid = blockIdx.x;
-  const int qt = nqt - 1 - bid / BH;  // longest (latest) query tiles first
-  const int bh = bid % BH;            // consecutive blocks: different heads
-  const int b = bh / H, hh = bh % H;
+  int qt, bh, b, hh;
+  if (PREFILL && B <= kPrefillOrderMaxB) {
+    // longest work first: sequences by cache offset, largest first (ties by index),
+    // then query tiles latest first, then heads.  Every workgroup ranks the B offsets
+    // itself; the ranks are a permutation, so exactly one sequence matches.
+    __shared__ int pick;
+    const int per_seq = nqt * H;
+    const int want = bid / per_seq;
+    for (int bb = threadIdx.x; bb < B; bb += blockDim.x) {
+      const int ob = min(max(seqlens[bb], 0), Tkv - T);
+      int r = 0;
+      for (int j = 0; j < B; ++j) {
+        const int oj = min(max(seqlens[j], 0), Tkv - T);
+        r += (oj > ob) || (oj == ob && j < bb);
+      }
+      if (r == want) pick = bb;
+    }
+    __syncthreads();
+    b = pick;
+    const int rem = bid - want * per_seq;
+    qt = nqt - 1 - rem / H;
+    hh = rem % H;
+    bh = b * H + hh;
+  } else {
+    qt = nqt - 1 - bid / BH;  // longest (latest) query tiles first
+    bh = bid % BH;            // consecutive blocks: different heads
+    b = bh / H;
+    hh = bh % H;
+  }
   // positions of the chunk's queries start at off; keys 0 .. Tk - 1 are in view
   const int off = PREFILL ? min(max(seqlens[b], 0), Tkv - T) : 0;
   const int Tk = off + T;
