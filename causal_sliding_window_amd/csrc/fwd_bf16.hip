@@ -72,17 +72,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   if (PREFILL && B <= kPrefillOrderMaxB) {
     // longest work first: sequences by cache offset, largest first (ties by index),
     // then query tiles latest first, then heads.  Every workgroup ranks the B offsets
-    // itself; the ranks are a permutation, so exactly one sequence matches.
-    __shared__ int pick;
+    // itself from LDS; the ranks are a permutation, so exactly one sequence matches.
+    __shared__ int pick, offs[kPrefillOrderMaxB];
     const int per_seq = nqt * H;
     const int want = bid / per_seq;
+    for (int bb = threadIdx.x; bb < B; bb += blockDim.x)
+      offs[bb] = min(max(seqlens[bb], 0), Tkv - T);
+    __syncthreads();
     for (int bb = threadIdx.x; bb < B; bb += blockDim.x) {
-      const int ob = min(max(seqlens[bb], 0), Tkv - T);
+      const int ob = offs[bb];
       int r = 0;
-      for (int j = 0; j < B; ++j) {
-        const int oj = min(max(seqlens[j], 0), Tkv - T);
-        r += (oj > ob) || (oj == ob && j < bb);
-      }
+      for (int j = 0; j < B; ++j) r += (offs[j] > ob) || (offs[j] == ob && j < bb);
       if (r == want) pick = bb;
     }
     __syncthreads();
