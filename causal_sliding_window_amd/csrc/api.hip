@@ -48,6 +48,14 @@ int all_aligned(std::initializer_list<const void *> ps) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SWATTN_OK : SWATTN_ERR_HIP; }
 
+// The softmax scale must be a positive finite number: the kernels fold it into the
+// exponent and mask scores before scaling, which is only the masked softmax of
+// scale * Q K^T for scale > 0 (scale 0 would turn masked scores into NaN, a negative
+// one would give masked keys the largest weight).
+int check_scale(float scale) {
+  return (scale > 0.f && std::isfinite(scale)) ? SWATTN_OK : SWATTN_ERR_INVALID_ARG;
+}
+
 int check_decode(int B, int H, int D, int Tmax, int window) {
   if (B <= 0 || H <= 0 || D <= 0 || Tmax <= 0 || window == 0) return SWATTN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return SWATTN_ERR_UNSUPPORTED;
@@ -103,6 +111,7 @@ int bwd_all(bool bf16, const void *q, const void *k, const void *v, const void *
             int Hkv, int T, int D, int window, float scale, void *workspace, hipStream_t st) {
   int s = check_common(B, H, T, D, window);
   if (s == SWATTN_OK) s = check_group(H, Hkv);
+  if (s == SWATTN_OK) s = check_scale(scale);
   if (s != SWATTN_OK) return s;
   if (!all_aligned({q, k, v, o, dO, dq, dk, dv, workspace}) || lse == nullptr)
     return SWATTN_ERR_INVALID_ARG;
@@ -130,6 +139,7 @@ int bwd_dkdv(bool bf16, const void *q, const void *k, const void *v, const void 
              const float *lse, const void *workspace, void *dk, void *dv, int B, int H, int T,
              int D, int window, float scale, hipStream_t st) {
   int s = check_common(B, H, T, D, window);
+  if (s == SWATTN_OK) s = check_scale(scale);
   if (s != SWATTN_OK) return s;
   if (!all_aligned({q, k, v, dO, workspace, dk, dv}) || lse == nullptr)
     return SWATTN_ERR_INVALID_ARG;
@@ -141,6 +151,7 @@ int bwd_dq(bool bf16, const void *q, const void *k, const void *v, const void *o
            const void *dO, const float *lse, void *workspace, void *dq, int B, int H, int T,
            int D, int window, float scale, hipStream_t st) {
   int s = check_common(B, H, T, D, window);
+  if (s == SWATTN_OK) s = check_scale(scale);
   if (s != SWATTN_OK) return s;
   if (!all_aligned({q, k, v, o, dO, workspace, dq}) || lse == nullptr)
     return SWATTN_ERR_INVALID_ARG;
@@ -167,6 +178,7 @@ int swattn_version(void) { return kVersion; }
 int swattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                int T, int D, int window, float scale, swattn_stream_t stream) {
   int st = check_common(B, H, T, D, window);
+  if (st == SWATTN_OK) st = check_scale(scale);
   if (st != SWATTN_OK) return st;
   if (!all_aligned({q, k, v, o}) || lse == nullptr) return SWATTN_ERR_INVALID_ARG;
   return hip_status(swattn::launch_fwd_bf16(q, k, v, o, lse, B, H, H, T, D, window, scale,
@@ -178,6 +190,7 @@ int swattn_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *
                    swattn_stream_t stream) {
   int st = check_common(B, H, T, D, window);
   if (st == SWATTN_OK) st = check_group(H, Hkv);
+  if (st == SWATTN_OK) st = check_scale(scale);
   if (st != SWATTN_OK) return st;
   if (!all_aligned({q, k, v, o}) || lse == nullptr) return SWATTN_ERR_INVALID_ARG;
   return hip_status(swattn::launch_fwd_bf16(q, k, v, o, lse, B, H, Hkv, T, D, window, scale,
@@ -187,6 +200,7 @@ int swattn_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *
 int swattn_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse, int B,
                    int H, int T, int D, int window, float scale, swattn_stream_t stream) {
   int st = check_common(B, H, T, D, window);
+  if (st == SWATTN_OK) st = check_scale(scale);
   if (st != SWATTN_OK) return st;
   if (!all_aligned({q, k, v, o}) || lse == nullptr) return SWATTN_ERR_INVALID_ARG;
   return hip_status(swattn::launch_fwd_f32(q, k, v, o, lse, B, H, T, D, window, scale,
@@ -270,6 +284,7 @@ int swattn_prefill(const void *q, const void *k_new, const void *v_new, void *k_
                    swattn_stream_t stream) {
   int st = check_common(B, H, Tq, D, window);
   if (st == SWATTN_OK) st = check_group(H, Hkv);
+  if (st == SWATTN_OK) st = check_scale(scale);
   if (st != SWATTN_OK) return st;
   if (Tmax <= 0 || Tq > Tmax) return SWATTN_ERR_INVALID_ARG;
   // the caches: 32-bit grid/row indices and 32-bit buffer offsets per sequence
@@ -295,6 +310,7 @@ static int decode_common(bool bf16, const void *q, const void *k_cache, const vo
                          swattn_stream_t stream) {
   int st = check_decode(B, H, D, Tmax, window);
   if (st == SWATTN_OK) st = check_group(H, Hkv);
+  if (st == SWATTN_OK) st = check_scale(scale);
   if (st != SWATTN_OK) return st;
   if (!all_aligned({q, k_cache, v_cache, o, workspace}) || seqlens == nullptr)
     return SWATTN_ERR_INVALID_ARG;

@@ -65,6 +65,14 @@ struct DqCfg {
   static constexpr int RG = BN / 16;           // 16-row groups per 32-column block
 };
 
+// Largest |dS| of a tile (any lane) from which dS enters dQ as bf16 hi + lo, and the
+// head sizes that take that path.  At D = 128 the kernel holds 254 of its 256 VGPRs
+// and every arrangement of the lo products tried spills, so there dS always enters as
+// one bf16 (the D = 128 sweeps meet the bar with it).
+constexpr float kLoDs = 1.0f;
+template <int D>
+constexpr bool kDsLo = D == 64;
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -181,8 +189,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     }
   };
 
-  // dS = P (dP - delta) for elements [e0, e0 + n) of a tile (into dp).
-  auto ds_elems = [&](auto mask_tag, f32x16 &s, f32x16 &dp, int rel0, int e0, int n) {
+  // dS = P (dP - delta) for elements [e0, e0 + n) of a tile (into dp); dm keeps the
+  // largest |dS| of the lane (only where the lo path exists).
+  auto ds_elems = [&](auto mask_tag, f32x16 &s, f32x16 &dp, float &dm, int rel0, int e0, int n) {
     constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
     for (int i = e0; i < e0 + n; ++i) {
@@ -190,21 +199,45 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
       if (MASK) p = (unsigned)(rel0 - c_row(i, 0)) <= wm1 ? p : 0.f;
       dp[i] = p * (dp[i] - dl);
     }
+    if constexpr (kDsLo<D>) {
+#pragma unroll
+      for (int i = e0; i < e0 + n; i += 2) dm = fmaxf(dm, fmaxf(fabsf(dp[i]), fabsf(dp[i + 1])));
+    }
   };
   // dQ^T += K^T dS^T for a tile (K^T by one asm block of transposed reads, so the
-  // copies in flight are not waited for)
-  auto dq_from = [&](const bf16x8 (&kt_op)[2][C::NDB], const f32x16 &ds) {
+  // copies in flight are not waited for).  dS enters as one bf16 (nearest even) unless
+  // some |dS| of the wave's tile reaches kLoDs (D = 64); then as hi + lo, hi = dS
+  // rounded and lo = the remainder rounded (dS = hi + lo to ~2^-17 relative).  With one
+  // bf16 dS everywhere, large |dS| (peaked rows) move |dq| ~ 4..8 by up to 0.02 against
+  // the exact gradient together with the bf16 output's own half ulp.
+  auto dq_from = [&](const bf16x8 (&kt_op)[2][C::NDB], const f32x16 &ds, float dm, int kt) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const bf16x8 dsb = to_bf16x8(ds, 8 * t);
 #pragma unroll
       for (int d = 0; d < C::NDB; ++d) acc[d] = mfma32(kt_op[t][d], dsb, acc[d]);
     }
+    if (kDsLo<D> && __builtin_amdgcn_ballot_w64(dm >= kLoDs) != 0) {
+      // the K^T operands are read again (tile kt stays in LDS until the next step)
+      bf16x8 kt_op2[2][C::NDB];
+      dt_read_tr_perm_block<C::BN, C::NDB>(k_tile(kt), 0, lane, kt_op2);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float hi = (float)(__bf16)ds[8 * t + j];
+          lo[j] = (__bf16)(ds[8 * t + j] - hi);
+        }
+#pragma unroll
+        for (int d = 0; d < C::NDB; ++d) acc[d] = mfma32(kt_op2[t][d], lo, acc[d]);
+      }
+    }
   };
-  auto dq_mfma = [&](int kt, const f32x16 &ds) {
+  auto dq_mfma = [&](int kt, const f32x16 &ds, float dm) {
     bf16x8 kt_op[2][C::NDB];
     dt_read_tr_perm_block<C::BN, C::NDB>(k_tile(kt), 0, lane, kt_op);
-    dq_from(kt_op, ds);
+    dq_from(kt_op, ds, dm, kt);
   };
   auto pin = [](float x) {
     asm volatile("" ::"v"(x));
@@ -235,6 +268,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);
     const int rel0 = my_q - kt * C::BN - 8 * h;
     constexpr int EPS = 16 / C::KST;  // elements per slice
+    float dm = 0.f;
     bf16x8 kt_op[2][C::NDB];
     constexpr int TR0 = C::KST / 2;  // first slice with K^T reads (two operands each)
 #pragma unroll
@@ -251,10 +285,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
       sn = mfma32(ka[st], qr[st], st ? sn : f32x16{});
       dpn = mfma32(va[st], gr[st], st ? dpn : f32x16{});
       __builtin_amdgcn_sched_barrier(0);
-      ds_elems(mask_tag, sc, dpc, rel0, EPS * st, EPS);
+      ds_elems(mask_tag, sc, dpc, dm, rel0, EPS * st, EPS);
       pin(dpc[EPS * st + EPS - 1]);
     }
-    dq_from(kt_op, dpc);
+    dq_from(kt_op, dpc, dm, kt);
   };
   auto step = [&](auto mask_tag, int kt, f32x16 &sc, f32x16 &dpc, f32x16 &sn, f32x16 &dpn)
       __attribute__((always_inline)) {
@@ -262,8 +296,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   };
   auto last_step = [&](int kt, f32x16 &sc, f32x16 &dpc) {
     issue(kt + C::AHEAD);
-    ds_elems(std::true_type{}, sc, dpc, my_q - kt * C::BN - 8 * h, 0, 16);
-    dq_mfma(kt, dpc);
+    float dm = 0.f;
+    ds_elems(std::true_type{}, sc, dpc, dm, my_q - kt * C::BN - 8 * h, 0, 16);
+    dq_mfma(kt, dpc, dm);
   };
   // End of step kt: tile kt + 2 (copied a step earlier) must have landed; the copies
   // of this step (tile kt + AHEAD) may stay in flight.  Before every step kt, tiles

@@ -41,6 +41,12 @@ struct DkdvCfg {
 
 // Largest P of a tile (any lane) from which P enters dV as bf16 hi + lo.
 constexpr float kLoP = 0.0625f;
+// Largest |dS| of a tile (any lane) from which dS enters dK as bf16 hi + lo, and the head
+// sizes that take that path (D = 128 has no registers to spare for it; its sweeps meet
+// the bar with one bf16 dS).
+constexpr float kLoDsK = 1.0f;
+template <int D>
+constexpr bool kDsLoK = D == 64;
 
 // PARTIAL (grouped-query attention, H > Hkv): the workgroup's query head is one of
 // the G = H / Hkv that read K/V head h / G; it writes its fp32 contributions to dK
@@ -193,8 +199,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 
   // P = exp2(c S') and dS = P dP' for elements [e0, e0 + n) of a tile; pm keeps the
   // largest P of the lane.
-  auto grad_elems = [&](auto mask_tag, f32x16 &s, f32x16 &dp, float &pm, int rel0, int e0,
-                        int n) {
+  auto grad_elems = [&](auto mask_tag, f32x16 &s, f32x16 &dp, float &pm, float &dm, int rel0,
+                        int e0, int n) {
     constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
     for (int i = e0; i < e0 + n; ++i) {
@@ -206,6 +212,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     }
 #pragma unroll
     for (int i = e0; i < e0 + n; i += 2) pm = fmaxf(pm, fmaxf(s[i], s[i + 1]));
+    if constexpr (kDsLoK<D>) {
+#pragma unroll
+      for (int i = e0; i < e0 + n; i += 2) dm = fmaxf(dm, fmaxf(fabsf(dp[i]), fabsf(dp[i + 1])));
+    }
+  };
+  // dS enters dK as one bf16 unless some |dS| of the wave's tile reaches kLoDsK (D = 64):
+  // then also its remainder, lo = dS - bf16(dS) rounded to bf16.
+  auto pack_ds_lo = [&](const f32x16 &dp, int t) {
+    bf16x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (__bf16)(dp[8 * t + j] - (float)(__bf16)dp[8 * t + j]);
+    return r;
+  };
+  auto grads_ds_lo = [&](const bf16x8 (&ops)[2 * C::NDB], const bf16x8 &dl) {
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d) dka[d] = mfma32(ops[C::NDB + d], dl, dka[d]);
   };
   // P enters dV as bf16.  Where some P of the wave's tile reaches kLoP, it enters as
   // hi + lo instead: hi = P truncated to bf16, lo = the exact remainder rounded to
@@ -267,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     issue_to(qt + C::AHEAD, dma, vdma);
     const int rel0 = qt * C::BQ + 8 * h - my_k;
     bf16x8 op0[2 * C::NDB], op1[2 * C::NDB];
-    float pm = 0.f;
+    float pm = 0.f, dm = 0.f;
     if constexpr (NEXT) {
       const bf16x8 av = bcast_op(xv);
       sn = mfma32(av, bsel_s, f32x16{});
@@ -283,12 +305,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
         dpn = mfma32(ga[st], vr[st], dpn);
       }
       __builtin_amdgcn_sched_barrier(0);
-      grad_elems(mask_tag, sc, dpc, pm, rel0, EPS * st, EPS);
+      grad_elems(mask_tag, sc, dpc, pm, dm, rel0, EPS * st, EPS);
       pin(dpc[EPS * st + EPS - 1]);
     }
     // phases 2a and 2b; the lo part of P only where the tile holds a large P, its
     // MFMAs grouped after each phase (one branch per group)
     const bool lo = __builtin_amdgcn_ballot_w64(pm >= kLoP) != 0;
+    const bool lods = kDsLoK<D> && __builtin_amdgcn_ballot_w64(dm >= kLoDsK) != 0;
     bf16x8 ph0, pl0, ph1, pl1;
     if (lo) {
       pack_hilo(sc, 0, ph0, pl0);
@@ -310,6 +333,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     if (lo) grads_lo(op0, pl0);
+    if (lods) grads_ds_lo(op0, pack_ds_lo(dpc, 0));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int d = 0; d < C::NDB; ++d) {
@@ -326,6 +350,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     if (lo) grads_lo(op1, pl1);
+    if (lods) grads_ds_lo(op1, pack_ds_lo(dpc, 1));
   };
   auto step = [&](auto mask_tag, auto next_tag, auto load_tag, int qt, f32x16 &sc, f32x16 &dpc,
                   f32x16 &sn, f32x16 &dpn, bf16x8 (&qa)[C::KST], bf16x8 (&ga)[C::KST],

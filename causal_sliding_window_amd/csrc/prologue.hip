@@ -28,7 +28,9 @@ constexpr int kPrologueRows = 4;  // token rows per wave
 
 template <int D, bool BWD>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *dq_in,
+    // no __restrict__ on the tensors: q_out may be q, k_out k, and in the backward the
+    // outputs may be dq_in, dk_in (in place)
+    const uint16_t *q, const uint16_t *k, const uint16_t *dq_in,
     const uint16_t *dk_in, uint16_t *q_out, uint16_t *k_out, const int *__restrict__ pos_off,
     int T, int H, int Hkv, int nrows, float base, float eps) {
   constexpr int LPV = D / 8;     // lanes per vector

@@ -49,6 +49,10 @@
  *
  * Errors: every entry point returns a swattn_status; nothing is thrown.
  *   SWATTN_ERR_INVALID_ARG  NULL required pointer, B/H/T/D/Tmax <= 0, window == 0,
+ *                           scale not a positive finite number (every call that
+ *                           takes a scale: the masked softmax of scale * QK^T is
+ *                           computed with the mask applied before the scale, which
+ *                           equals masking after it only for scale > 0),
  *                           Hkv <= 0 or not dividing H (*_gqa),
  *                           a size product that does not fit the kernels' 32-bit
  *                           grid/row indices, or a workspace pointer of NULL

@@ -25,6 +25,17 @@ def errors(got, ref):
     return max_abs, rel, float(np.abs(ref[mask]).max()) if d.size else 0.0
 
 
+def bf16_ulps(got, ref):
+    """Largest error in units of the bf16 spacing at |ref| (2^(e - 7) for |ref| in
+    [2^e, 2^(e+1)); the smallest normal's spacing below that)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    mask = ~np.isnan(ref)
+    a = np.maximum(np.abs(ref[mask]), 2.0 ** -126)
+    ulp = 2.0 ** (np.floor(np.log2(a)) - 7)
+    return float((np.abs(got[mask] - ref[mask]) / ulp).max()) if a.size else 0.0
+
+
 def check(name, got, ref, dtype, lse=False, out_ulp=False):
     """Assert the tolerance for one output; returns (max_abs, rel_l2).
 
@@ -38,9 +49,13 @@ def check(name, got, ref, dtype, lse=False, out_ulp=False):
     if out_ulp and dtype == torch.bfloat16:
         mask = ~np.isnan(ref)
         excess = float((np.abs(got[mask] - ref[mask]) - 2.0 ** -9 * np.abs(ref[mask])).max())
+        ulps = bf16_ulps(got, ref)
         assert excess <= TOL_BF16_ABS, (
-            f"{name}: max(|err| - 2^-9 |ref|) {excess:.3e} > {TOL_BF16_ABS} (|ref| <= {ref_max:.2f})")
-        assert rel <= TOL_BF16_REL, f"{name}: rel-L2 {rel:.3e} > {TOL_BF16_REL}"
+            f"{name}: max(|err| - 2^-9 |ref|) {excess:.3e} > {TOL_BF16_ABS} (|ref| <= {ref_max:.2f}, "
+            f"max-abs {max_abs:.3e} = {ulps:.1f} bf16 ulps of |ref|)")
+        assert rel <= TOL_BF16_REL, (
+            f"{name}: rel-L2 {rel:.3e} > {TOL_BF16_REL} (max-abs {max_abs:.3e} = {ulps:.1f} bf16 "
+            f"ulps of |ref|)")
         return max_abs, rel
     if dtype == torch.float32:
         assert max_abs <= TOL_F32, f"{name}: max-abs {max_abs:.3e} > {TOL_F32} (|ref| <= {ref_max:.2f})"
@@ -70,3 +85,23 @@ def only_heads(a, heads, layout="bthd"):
         else:  # bht
             out[b, h, :] = a[b, h, :]
     return out
+
+
+# ----------------------------------------------------------------------------- edge sweep
+# Ragged lengths, windows with edges inside a 32-row tile, both head sizes; inputs drawn
+# like the training workloads (q, k RMS-normalised).
+EDGE_T = (1, 2, 63, 129, 300, 520)
+EDGE_W = (-1, 1, 63, 65, 129, 256)
+EDGE_D = (64, 128)
+
+
+def edge_inputs(inputs, T, W, D):
+    return inputs.training_inputs(2, T, 3, D, "bf16", seed=7 * T + W, qk_norm=True)
+
+
+# Edge cases where the oracle's own gradient misses the bf16 bar against the exact
+# gradient once delta is formed from the bf16-rounded exact o, i.e. where rounding the
+# forward's output alone uses up the bar (T = 2: dq and dk are tiny against the
+# rounding of delta = dO . o).  tests/test_rounding_floor.py derives this set on the CPU;
+# the composed GPU test skips exactly these cases.
+COMPOSED_ROUNDING_MISSES = {(2, 63, 64)}

@@ -143,3 +143,27 @@ def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(swattn.SwattnError):
         swattn.fwd(q, q, q)
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0, float("nan"), float("inf"), -0.0])
+def test_scale_must_be_positive_and_finite(scale):
+    """Every call that takes a softmax scale rejects one that is not a positive finite
+    number, before anything launches (the kernels apply the mask before the scale)."""
+    lib = swattn.lib()
+    p5, p6, p8, p9 = [FAKE] * 5, [FAKE] * 6, [FAKE] * 8, [FAKE] * 9
+    assert lib.swattn_fwd(*p5, 1, 1, 8, 64, -1, scale, None) == 1
+    assert lib.swattn_fwd_f32(*p5, 1, 1, 8, 64, 4, scale, None) == 1
+    assert lib.swattn_fwd_gqa(*p5, 1, 6, 3, 8, 64, -1, scale, None) == 1
+    assert lib.swattn_bwd(*p9, 1, 1, 8, 64, -1, scale, FAKE, None) == 1
+    assert lib.swattn_bwd_f32(*p9, 1, 1, 8, 64, -1, scale, FAKE, None) == 1
+    assert lib.swattn_bwd_gqa(*p9, 1, 6, 3, 8, 64, -1, scale, FAKE, None) == 1
+    assert lib.swattn_bwd_dq(*p8, 1, 1, 8, 64, -1, scale, None) == 1
+    assert lib.swattn_bwd_dkdv(*p8, 1, 1, 8, 64, -1, scale, None) == 1
+    assert lib.swattn_bwd_dq_f32(*p8, 1, 1, 8, 64, -1, scale, None) == 1
+    assert lib.swattn_bwd_dkdv_f32(*p8, 1, 1, 8, 64, -1, scale, None) == 1
+    assert lib.swattn_decode(*p6, 1, 1, 128, 16, -1, scale, FAKE, None) == 1
+    assert lib.swattn_decode_f32(*p6, 1, 1, 128, 16, 8, scale, FAKE, None) == 1
+    assert lib.swattn_decode_gqa(*p6, 1, 6, 2, 128, 16, -1, scale, FAKE, None) == 1
+    # q, k_new, v_new, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, Tq, D, Tmax, W, scale
+    assert lib.swattn_prefill(*p8, 1, 2, 2, 8, 64, 16, -1, scale, None) == 1
+

@@ -14,7 +14,8 @@ import torch
 
 from causal_sliding_window_amd import inputs, swattn
 from oracle import attention as orc
-from parity import check, f64, only_heads, sample_heads
+from parity import (COMPOSED_ROUNDING_MISSES, EDGE_D, EDGE_T, EDGE_W, check, edge_inputs, f64,
+                    only_heads, sample_heads)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -84,14 +85,33 @@ def test_fp32_shapes(T, D, W):
 
 
 # ----------------------------------------------------------------------------- bf16, small shapes
-@pytest.mark.parametrize("T", [1, 2, 63, 129, 300, 520])
-@pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("W", [-1, 1, 63, 65, 129, 256])
+@pytest.mark.parametrize("T", EDGE_T)
+@pytest.mark.parametrize("D", EDGE_D)
+@pytest.mark.parametrize("W", EDGE_W)
 def test_bf16_shapes(T, D, W):
-    """Ragged lengths and window edges mid-tile, inputs drawn like the training workloads."""
-    x = inputs.training_inputs(2, T, 3, D, "bf16", seed=7 * T + W, qk_norm=True)
+    """Ragged lengths and window edges mid-tile, inputs drawn like the training workloads;
+    each stage in isolation (the backward gets the oracle's o and LSE)."""
+    x = edge_inputs(inputs, T, W, D)
     scale = 1 / math.sqrt(D)
     compare_all(*run_entry_points(x, W, scale), torch.bfloat16)
+
+
+@pytest.mark.parametrize("T", EDGE_T)
+@pytest.mark.parametrize("D", EDGE_D)
+@pytest.mark.parametrize("W", EDGE_W)
+def test_bf16_shapes_composed(T, D, W):
+    """The same sweep composed as a training step runs it: GPU forward, then the GPU
+    backward fed that forward's o and LSE, every output against the exact gradient of
+    the exact forward.  Cases where rounding o to bf16 alone already puts the oracle's
+    own gradient outside the bar (derived on the CPU in tests/test_rounding_floor.py)
+    are skipped."""
+    if (T, W, D) in COMPOSED_ROUNDING_MISSES:
+        pytest.skip("rounding o to bf16 alone moves the exact gradient outside the bar "
+                    "(tests/test_rounding_floor.py)")
+    x = edge_inputs(inputs, T, W, D)
+    scale = 1 / math.sqrt(D)
+    compare_all(run_fwd_bwd(_gpu(x), W, scale), oracle_fwd_bwd(x, W, scale), torch.bfloat16,
+                tag=f"T{T} W{W} D{D} ")
 
 
 def test_bf16_raw_normal_qk():

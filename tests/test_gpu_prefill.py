@@ -121,3 +121,21 @@ def test_prefill_rejects_bad_sizes():
     seq = torch.zeros(1, dtype=torch.int32, device=DEV)
     with pytest.raises(swattn.SwattnError):
         swattn.prefill(q, q, q, kc, kc.clone(), seq)
+
+
+@pytest.mark.parametrize("B", [256, 257])
+def test_prefill_many_sequences_work_order(B):
+    """The prefill grid ranks up to 256 sequences by cache offset on the device (largest
+    first, ties by index) and falls back to plain order beyond.  B = 256 with many tied
+    offsets fills the ranking table to its limit; B = 257 takes the fallback.  Tiny
+    chunks (Tq 33, H 2, D 64) keep the oracle fast; every sequence is compared."""
+    rng = np.random.default_rng(B)
+    lens = rng.choice([0, 5, 37, 64, 64, 64, 100], size=B)  # many equal offsets
+    x = _case(B, 33, 2, 1, 64, 160, lens, seed=B)
+    scale = 1 / math.sqrt(64)
+    for W in (-1, 40):
+        o, lse, kc, vc = _run(x, W, scale)  # on device copies: x keeps the old caches
+        ro, rl, rkc, rvc = _oracle(x, W, scale)
+        check(f"B{B} W{W} o", o, ro, torch.bfloat16)
+        check(f"B{B} W{W} lse", lse, rl, torch.bfloat16, lse=True)
+        assert np.array_equal(inputs.to_f64(kc), rkc) and np.array_equal(inputs.to_f64(vc), rvc)
