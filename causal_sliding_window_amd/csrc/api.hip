@@ -169,6 +169,7 @@ const char *swattn_status_string(int status) {
     case SWATTN_ERR_INVALID_ARG: return "SWATTN_ERR_INVALID_ARG";
     case SWATTN_ERR_UNSUPPORTED: return "SWATTN_ERR_UNSUPPORTED";
     case SWATTN_ERR_HIP: return "SWATTN_ERR_HIP";
+    case SWATTN_ERR_TOO_LARGE: return "SWATTN_ERR_TOO_LARGE";
     default: return "SWATTN_ERR_UNKNOWN";
   }
 }
@@ -331,6 +332,30 @@ int swattn_decode_gqa(const void *q, const void *k_cache, const void *v_cache, c
                       float scale, void *workspace, swattn_stream_t stream) {
   return decode_common(true, q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, D, Tmax, window,
                        scale, workspace, stream);
+}
+
+int swattn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                          const int *seqlens, void *o, float *lse, int B, int H, int D, int Tmax,
+                          int window, float scale, swattn_stream_t stream) {
+  // every argument check of swattn_decode first, then the scratch bound: nothing here
+  // touches the GPU before the arguments are known to be valid
+  int st = check_decode(B, H, D, Tmax, window);
+  if (st == SWATTN_OK) st = check_scale(scale);
+  if (st != SWATTN_OK) return st;
+  if (!all_aligned({q, k_cache, v_cache, o}) || seqlens == nullptr) return SWATTN_ERR_INVALID_ARG;
+  if (swattn_decode_workspace_size(B, H, D, Tmax, window) > swattn::kNoAllocScratchBytes)
+    return SWATTN_ERR_TOO_LARGE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SWATTN_ERR_HIP;
+  if (stream != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return SWATTN_ERR_HIP;
+    if (sdev != dev) return SWATTN_ERR_INVALID_ARG;  // the stream's device must be current
+  }
+  void *ws = swattn::noalloc_scratch(dev);
+  if (ws == nullptr) return SWATTN_ERR_HIP;
+  return decode_common(true, q, k_cache, v_cache, seqlens, o, lse, B, H, H, D, Tmax, window,
+                       scale, ws, stream);
 }
 
 int swattn_decode_f32(const float *q, const float *k_cache, const float *v_cache,

@@ -14,6 +14,12 @@ constexpr int kDecodeHeadBatch = 16;
 
 int decode_num_splits(int Tmax, int window);
 
+// Allocation-free decode (noalloc.hip): the size of the per-device scratch array, and
+// its device address on `device`, which must be the current device (looked up on the
+// first call for that device, then cached; nullptr on a HIP error).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+void *noalloc_scratch(int device);
+
 // Hkv: K/V heads (H, or a divisor of H: query head h reads K/V head h / (H / Hkv)).
 // The fp32 kernels take no Hkv (they serve H == Hkv only).
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,

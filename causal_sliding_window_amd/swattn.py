@@ -45,6 +45,7 @@ _SIGS = {
     "swattn_decode_workspace_size": ([_I] * 5, ctypes.c_size_t),
     "swattn_decode": ([_P] * 6 + [_I] * 5 + [_F, _P, _P], _I),
     "swattn_decode_f32": ([_P] * 6 + [_I] * 5 + [_F, _P, _P], _I),
+    "swattn_decode_noalloc": ([_P] * 6 + [_I] * 5 + [_F, _P], _I),
     "swattn_fwd_gqa": ([_P] * 5 + [_I] * 6 + [_F, _P], _I),
     "swattn_bwd_gqa_workspace_size": ([_I] * 5, ctypes.c_size_t),
     "swattn_bwd_gqa": ([_P] * 9 + [_I] * 6 + [_F, _P, _P], _I),
@@ -226,6 +227,25 @@ def swattn_decode(q, k_cache, v_cache, seqlens, o, lse, window: int, scale: floa
 
 
 swattn_decode_f32 = swattn_decode
+
+
+def swattn_decode_noalloc(q, k_cache, v_cache, seqlens, o, lse, window: int, scale: float,
+                          stream=None):
+    """Allocation-free decode (bf16): as swattn_decode, with the library's own scratch
+    array instead of a workspace (no device allocation anywhere in the call)."""
+    B, H, D = q.shape
+    Tmax = k_cache.shape[1]
+    for n, t, shape in (("q", q, (B, H, D)), ("o", o, (B, H, D)),
+                        ("k_cache", k_cache, (B, Tmax, H, D)),
+                        ("v_cache", v_cache, (B, Tmax, H, D))):
+        _dev_tensor(t, n, torch.bfloat16, shape)
+    _dev_tensor(seqlens, "seqlens", torch.int32, (B,))
+    if lse is not None:
+        _dev_tensor(lse, "lse", torch.float32, (B, H))
+    _check(lib().swattn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens),
+                                       _ptr(o), _ptr(lse), B, H, D, Tmax, int(window),
+                                       float(scale), _stream(stream, q.device)),
+           "swattn_decode_noalloc")
 
 
 # ----------------------------------------------------------------------------- grouped-query entries

@@ -78,7 +78,8 @@ typedef enum {
   SWATTN_OK = 0,
   SWATTN_ERR_INVALID_ARG = 1,
   SWATTN_ERR_UNSUPPORTED = 2,
-  SWATTN_ERR_HIP = 3
+  SWATTN_ERR_HIP = 3,
+  SWATTN_ERR_TOO_LARGE = 4 /* swattn_decode_noalloc: the sizes need more scratch than it has */
 } swattn_status;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -210,6 +211,27 @@ int swattn_decode_f32(const float *q, const float *k_cache,
                       const float *v_cache, const int *seqlens, float *o,
                       float *lse, int B, int H, int D, int Tmax, int window,
                       float scale, void *workspace, swattn_stream_t stream);
+/*
+ * Allocation-free decode, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * swattn_decode (same kernels, same results, bitwise), with its partials kept in a
+ * scratch array that the library holds in device memory instead of a workspace.
+ * The array holds SWATTN_NOALLOC_SCRATCH_BYTES (16 MiB) on every GPU the library runs
+ * on, from that GPU's first call until the process ends.  The call allocates nothing
+ * and frees nothing; the first call on a device looks up the array's address there
+ * (that device must be current; a non-NULL stream must belong to it).
+ * Sizes whose swattn_decode_workspace_size() exceeds the array return
+ * SWATTN_ERR_TOO_LARGE before anything is enqueued (e.g. B*H = 384 heads fit up to
+ * Tmax = 8192 or any window <= 8192 at D = 128).  Every call on one GPU shares that
+ * GPU's array: calls that may run at the same time on one GPU (other streams, other
+ * threads) race on it and must be serialised by the caller.  Nothing in the array
+ * needs to start at zero.  Other errors as swattn_decode.
+ */
+#define SWATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+int swattn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                          const int *seqlens, void *o, float *lse, int B, int H, int D,
+                          int Tmax, int window, float scale, swattn_stream_t stream);
+
 /* Grouped-query decode (bf16): k_cache, v_cache [B,Tmax,Hkv,D]; each cache row is
  * read once for the H / Hkv query heads of its group.  The workspace is
  * swattn_decode_workspace_size(B, H, D, Tmax, window) bytes (partials per query

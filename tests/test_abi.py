@@ -167,3 +167,22 @@ def test_scale_must_be_positive_and_finite(scale):
     # q, k_new, v_new, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, Tq, D, Tmax, W, scale
     assert lib.swattn_prefill(*p8, 1, 2, 2, 8, 64, 16, -1, scale, None) == 1
 
+
+
+def test_noalloc_decode_checks_before_touching_the_gpu():
+    """swattn_decode_noalloc validates its arguments and its scratch bound before any HIP
+    call, so all of these return without a GPU."""
+    lib = swattn.lib()
+    p6 = [FAKE] * 6
+    assert swattn.status_string(4) == "SWATTN_ERR_TOO_LARGE"
+    # q, k_cache, v_cache, seqlens, o, lse, B, H, D, Tmax, window, scale, stream
+    assert lib.swattn_decode_noalloc(*p6, 1, 1, 128, 16, 0, 1.0, None) == 1     # window 0
+    assert lib.swattn_decode_noalloc(*p6, 1, 1, 96, 16, -1, 1.0, None) == 2     # D
+    assert lib.swattn_decode_noalloc(*p6, 1, 1, 128, 16, -1, 0.0, None) == 1    # scale
+    assert lib.swattn_decode_noalloc(FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 1, 128, 16, -1, 1.0,
+                                     None) == 1                                   # NULL seqlens
+    # 32 x 12 heads, 20000-row caches: 157 splits of 129 floats each, 31 MB > 16 MiB
+    assert swattn.swattn_decode_workspace_size(32, 12, 128, 20000, -1) > 16 << 20
+    assert lib.swattn_decode_noalloc(*p6, 32, 12, 128, 20000, -1, 1.0, None) == 4
+    # the decode workload (4096-row caches) fits: 6.3 MB
+    assert swattn.swattn_decode_workspace_size(32, 12, 128, 4096, -1) <= 16 << 20
