@@ -32,15 +32,15 @@ HIPCC_FLAGS = [
     # per-kernel register / scratch report, checked below
     "-Rpass-analysis=kernel-resource-usage",
 ]
-# Per-source extra flags.  Most kernels keep MFMA results in arch VGPRs, where
-# they feed ALU work (avoids accumulator <-> VGPR copies); the dK/dV kernel keeps
-# its accumulators in AGPRs, leaving the arch VGPRs to its operands.
+# Per-source extra flags.  The kernels keep MFMA results in arch VGPRs, where they
+# feed ALU work (avoids accumulator <-> VGPR copies).
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-EXTRA_FLAGS = {s: VGPR_FORM for s in SOURCES if s != "dkdv_bf16.hip"}
-# The forward's row maxima are taken over MFMA results, which are never NaN.  Without
-# this flag every fmaxf operand is first quieted (one extra v_max per element) and the
-# three-input v_max3 is not formed.
+EXTRA_FLAGS = {s: VGPR_FORM for s in SOURCES}
+# The forward's row maxima and the dK/dV pass's largest P are taken over MFMA results
+# and exponentials, which are never NaN.  Without this flag every fmaxf operand is
+# first quieted (one extra v_max per element) and the three-input v_max3 is not formed.
 EXTRA_FLAGS["fwd_bf16.hip"] = VGPR_FORM + ["-fno-honor-nans"]
+EXTRA_FLAGS["dkdv_bf16.hip"] = VGPR_FORM + ["-fno-honor-nans"]
 
 
 def hipcc() -> str:

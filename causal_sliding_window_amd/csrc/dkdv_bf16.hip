@@ -25,35 +25,54 @@ namespace swattn {
 // ---------------------------------------------------------------- dK, dV
 template <int D>
 struct DkdvCfg {
-  static constexpr int BK = 128;          // keys per workgroup (4 waves x 32)
+  static constexpr int BK = 128;          // keys per workgroup (4 key groups x 32)
   static constexpr int BQ = 32;           // queries per tile
-  static constexpr int NSLOT = 8;         // LDS tile slots (tile t in slot t % 8)
-  static constexpr int AHEAD = 6;         // tiles are copied this many steps ahead
+  static constexpr int NW = 8;            // waves: 4 P side + 4 dS side
+  static constexpr int NSLOT = 4;         // LDS tile slots (tile t in slot t % 4)
+  static constexpr int AHEAD = 2;         // tiles are copied this many steps ahead
   static constexpr int TSZ = BQ * D;      // elements of one Q (or dO) tile
   static constexpr int NDB = D / 32;
   static constexpr int KST = D / 16;      // = 2 * NDB
   static constexpr int HALF = TSZ * 2 / 1024;  // 1-KB pieces of one tensor's tile
-  static constexpr int CPW = 2 * HALF / 4;     // pieces per wave and tile (Q and dO)
+  static constexpr int CPW = 2 * HALF / NW;    // pieces per wave and tile (Q and dO)
   static constexpr int RG = BQ / 16;           // 16-row groups per 32-column block
   static constexpr int NCOPY = CPW + 1;        // copies per wave and tile (+ lse/delta)
-  static constexpr int VSZ = 256;              // floats of lse / delta per slot
+  static constexpr int VSZ = NW * 64;          // floats of lse / delta (and spares) per slot
+  static constexpr int XSZ = 16 * 64;          // floats of one handed-over P tile
+  static_assert(CPW >= 1 && (2 * HALF) % NW == 0, "whole 1-KB pieces per wave");
 };
 
 // Largest P of a tile (any lane) from which P enters dV as bf16 hi + lo.
 constexpr float kLoP = 0.0625f;
 // Largest |dS| of a tile (any lane) from which dS enters dK as bf16 hi + lo, and the head
-// sizes that take that path (D = 128 has no registers to spare for it; its sweeps meet
-// the bar with one bf16 dS).
+// sizes that take that path (at D = 128 the sweeps meet the bar with one bf16 dS).
 constexpr float kLoDsK = 1.0f;
 template <int D>
 constexpr bool kDsLoK = D == 64;
 
+// s_waitcnt immediate: at most N vector-memory operations in flight and every LDS
+// operation of the wave complete.
+template <int N>
+constexpr int kWaitVmLgkm0 = (N & 15) | ((N >> 4) << 14) | (7 << 4);
+
+// One workgroup = 8 waves = 128 keys of one (b, h), in 4 groups of 32 keys; each group
+// is served by two waves with the same keys (one per role), and the two run on the
+// same SIMD (waves g and g + 4):
+//   P side  (waves 0..3): S' = Q K^T - lse / scale, P = exp2(c S'), dV^T += dO^T P;
+//                         hands P (fp32) to its partner through LDS;
+//   dS side (waves 4..7): dP' = dO V^T - delta, and one step later, with the partner's
+//                         P of that tile, dS = P dP' and dK^T += Q^T dS.
+// Each wave holds one 32-key accumulator set (dV or dK, 64 registers) and one set of
+// stationary operands (K or V rows), so two waves fit one SIMD and each covers the
+// other's waits.  Query tiles of 32 rows reach LDS by direct buffer -> LDS copies,
+// two steps ahead; one workgroup barrier per step.
+//
 // PARTIAL (grouped-query attention, H > Hkv): the workgroup's query head is one of
 // the G = H / Hkv that read K/V head h / G; it writes its fp32 contributions to dK
 // (already scaled) and dV to part_k / part_v, [B, T, H, D], and dkdv_group_sum_kernel
 // adds the G of each K/V head.  Otherwise dk and dv are written directly.
 template <int D, bool PARTIAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, uint16_t *__restrict__ dk,
@@ -61,11 +80,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     int H, int Hkv, int T, int window, float scale, int nkt) {
   using C = DkdvCfg<D>;
   // One LDS array (with a single __shared__ variable the compiler keeps the restrict
-  // scopes below): [slot][Q, dO][TSZ] bf16, then [slot][lse, delta, spare, spare][64]
-  // float.
+  // scopes below): [slot][Q, dO][TSZ] bf16, then [slot][VSZ] float (lse, delta,
+  // spares), then [key group][2][XSZ] float (the handed-over P tiles).
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::NSLOT * 2 * C::TSZ +
-                                                          C::NSLOT * C::VSZ * 2];
+                                                          C::NSLOT * C::VSZ * 2 +
+                                                          4 * 2 * C::XSZ * 2];
   float *const vec = reinterpret_cast<float *>(smem + C::NSLOT * 2 * C::TSZ);
+  float *const xp = vec + C::NSLOT * C::VSZ;
 
   const int BH = B * H;
   const int bid = blockIdx.x;
@@ -83,12 +104,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in an SGPR
+  const int grp = w & 3;                                   // key group
+  const bool pside = w < 4;                                // role
   const int h = lane >> 5, ln = lane & 31;
-  const int kw0 = k0 + 32 * w;
+  const int kw0 = k0 + 32 * grp;
   const int my_k = kw0 + ln;
 
-  // query tiles of the workgroup and of this wave (a wave's keys kw0 .. kw0 + 31 are
-  // seen by queries kw0 .. kw0 + 31 + W - 1)
+  // query tiles of the workgroup and of this key group (keys kw0 .. kw0 + 31 are seen by
+  // queries kw0 .. kw0 + 31 + W - 1)
   const int k_last = min(T, k0 + C::BK) - 1;
   const int q_hi = window > 0 ? min(T - 1, k_last + window - 1) : T - 1;
   const int qt0 = k0 / C::BQ, qt1 = q_hi / C::BQ;
@@ -97,20 +120,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     wqt0 = kw0 / C::BQ;
     wqt1 = (window > 0 ? min(T - 1, kw0 + 31 + window - 1) : T - 1) / C::BQ;
   }
-  // tiles from mlo on hold a query past some key's window
+  // tile wqt0 holds the diagonal; tiles from mlo on hold a query past some key's window
   const int mlo = window > 0 ? (kw0 + window - 31 + C::BQ - 1) / C::BQ : (1 << 30);
   // query qq sees key my_k iff 0 <= qq - my_k <= wm1
   const unsigned wm1 = window > 0 ? (unsigned)(window - 1) : 0x7fffffffu;
 
-  // K and V rows of the wave's keys (B operands), rows past T read as zero; loaded
-  // in the prologue, between the tile copies
-  bf16x8 kr[C::KST], vr[C::KST];
-  f32x16 dka[C::NDB], dva[C::NDB];
+  // the stationary operand of the wave: K rows (P side) or V rows (dS side) of its keys
+  // (B operands; rows past T read as zero), and its accumulators (dV or dK)
+  bf16x8 kv[C::KST];
+  f32x16 acc[C::NDB];
 #pragma unroll
-  for (int d = 0; d < C::NDB; ++d) {
-    dka[d] = f32x16{};
-    dva[d] = f32x16{};
-  }
+  for (int d = 0; d < C::NDB; ++d) acc[d] = f32x16{};
   const float c = scale * kLog2e;
 
   // Copies of a Q and dO tile (rows in swap23 order, d-block-major, rows past T read
@@ -134,14 +154,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       buf_copy16_to_lds(rsrc_t, tile + my_tensor * C::TSZ + db * (C::BQ * 32) + row16 * 32,
                         lane_off + (uint32_t)(row16 * rs + 32 * db) * 2 + roff);
     }
-    // every wave issues exactly NCOPY copies per tile (waves 2 and 3 fill spare
-    // rows), so the end-of-step wait can count them
+    // every wave issues exactly NCOPY copies per tile (lse by even waves, delta by odd
+    // ones, each into its own 64 floats; waves 2..7 fill spares), so the end-of-step
+    // wait can count them
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc_v, (__attribute__((address_space(3))) void *)(vdst + w * 64), 4,
         (uint32_t)(lane + qt * C::BQ) * 4, 0, 0, 0);
   };
   auto q_tile = [&](int qt) { return smem + 2 * (qt & (C::NSLOT - 1)) * C::TSZ; };
   auto vec_of = [&](int qt) { return vec + (qt & (C::NSLOT - 1)) * C::VSZ; };
+  auto xp_of = [&](int qt) { return xp + (2 * grp + (qt & 1)) * C::XSZ; };
   auto issue = [&](int qt) { issue_to(qt, q_tile(qt), vec_of(qt)); };
 
   // lse and delta enter S and dP through one extra MFMA each.  MFMA row m of a tile
@@ -154,12 +176,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // = dP - delta gives dS = P dP'.
   const int vrow = 64 * h + swap23(ln);
   const float xmul = h ? -1.f : -1.f / scale;
-  bf16x8 bsel_s, bsel_d;
+  bf16x8 bsel;  // ones in K slots 0..2 (P side) or 8..10 (dS side)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    bsel_s[j] = (__bf16)((h == 0 && j < 3) ? 1.f : 0.f);
-    bsel_d[j] = (__bf16)((h == 1 && j < 3) ? 1.f : 0.f);
-  }
+  for (int j = 0; j < 8; ++j) bsel[j] = (__bf16)((h == (pside ? 0 : 1) && j < 3) ? 1.f : 0.f);
   auto bcast_op = [&](float xv) {
     const float x = xv * xmul;
     const __bf16 hi = (__bf16)x;
@@ -172,364 +191,223 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     a[2] = lo;
     return a;
   };
-
-  // S' and dP' of a tile, one key per lane: register 8t + j of half h holds query
-  // 16t + 8h + j of the tile.
-  auto sdp_from = [&](const bf16x8 (&qa)[C::KST], const bf16x8 (&ga)[C::KST], float xv,
-                      f32x16 &s, f32x16 &dp) {
-    const bf16x8 av = bcast_op(xv);
-    s = mfma32(av, bsel_s, f32x16{});
-    dp = mfma32(av, bsel_d, f32x16{});
+  // S' (P side: A = Q rows) or dP' (dS side: A = dO rows) of a tile, one key per lane:
+  // register 8t + j of half h holds query 16t + 8h + j of the tile.
+  auto sdp = [&](const uint16_t *__restrict__ rows, const float *__restrict__ vt, f32x16 &s) {
+    bf16x8 a[C::KST];
 #pragma unroll
-    for (int st = 0; st < C::KST; ++st) {
-      s = mfma32(qa[st], kr[st], s);
-      dp = mfma32(ga[st], vr[st], dp);
-    }
-  };
-  // Operand reads of a tile for S' / dP' (b128 rows) and the lane's lse / delta.
-  auto read_q = [&](const uint16_t *__restrict__ tile, int st) {
-    return lds_read_b128(tile + dt_off<C::BQ>(ln, 2 * st + h));
-  };
-  // Transposed operand k (k < NDB: dO^T block k, else Q^T block k - NDB) of rows
-  // 16 t .. 16 t + 15 of a tile.
-  auto tr_op = [&](const uint16_t *__restrict__ tile, int t, int kk) {
-    return dt_read_tr_perm<C::BQ>(kk < C::NDB ? tile + C::TSZ : tile, 16 * t, kk % C::NDB,
-                                  lane);
-  };
-
-  // P = exp2(c S') and dS = P dP' for elements [e0, e0 + n) of a tile; pm keeps the
-  // largest P of the lane.
-  auto grad_elems = [&](auto mask_tag, f32x16 &s, f32x16 &dp, float &pm, float &dm, int rel0,
-                        int e0, int n) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+    for (int st = 0; st < C::KST; ++st) a[st] = lds_read_b128(rows + dt_off<C::BQ>(ln, 2 * st + h));
+    s = mfma32(bcast_op(vt[vrow]), bsel, f32x16{});
 #pragma unroll
-    for (int i = e0; i < e0 + n; ++i) {
-      const int t = i >> 3, j = i & 7;
-      float p = fast_exp2(s[i] * c);
-      if (MASK) p = (unsigned)(rel0 + 16 * t + j) <= wm1 ? p : 0.f;
-      s[i] = p;
-      dp[i] = p * dp[i];
-    }
-#pragma unroll
-    for (int i = e0; i < e0 + n; i += 2) pm = fmaxf(pm, fmaxf(s[i], s[i + 1]));
-    if constexpr (kDsLoK<D>) {
-#pragma unroll
-      for (int i = e0; i < e0 + n; i += 2) dm = fmaxf(dm, fmaxf(fabsf(dp[i]), fabsf(dp[i + 1])));
-    }
+    for (int st = 0; st < C::KST; ++st) s = mfma32(a[st], kv[st], s);
   };
-  // dS enters dK as one bf16 unless some |dS| of the wave's tile reaches kLoDsK (D = 64):
-  // then also its remainder, lo = dS - bf16(dS) rounded to bf16.
-  auto pack_ds_lo = [&](const f32x16 &dp, int t) {
-    bf16x8 r;
+  // transposed operands (dO^T or Q^T) of rows 0..15 (t = 0) and 16..31 (t = 1)
+  using TrOps = bf16x8[2][C::NDB];
+  auto tr_ops = [&](const uint16_t *__restrict__ rows, TrOps &op) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = (__bf16)(dp[8 * t + j] - (float)(__bf16)dp[8 * t + j]);
-    return r;
-  };
-  auto grads_ds_lo = [&](const bf16x8 (&ops)[2 * C::NDB], const bf16x8 &dl) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int d = 0; d < C::NDB; ++d) dka[d] = mfma32(ops[C::NDB + d], dl, dka[d]);
+      for (int d = 0; d < C::NDB; ++d) op[t][d] = dt_read_tr_perm<C::BQ>(rows, 16 * t, d, lane);
   };
-  // P enters dV as bf16.  Where some P of the wave's tile reaches kLoP, it enters as
-  // hi + lo instead: hi = P truncated to bf16, lo = the exact remainder rounded to
-  // bf16 (P = hi + lo to ~2^-16 relative).  A single bf16 P on those large values
-  // leaves |dV| >= 4 outside 2e-2 of the exact gradient; below kLoP the rounding of
-  // P (<= 2^-13 absolute) is far inside it.
-  auto pack_rne = [&](const f32x16 &s, int t) { return to_bf16x8(s, 8 * t); };
-  auto pack_hilo = [&](const f32x16 &s, int t, bf16x8 &ph, bf16x8 &pl) {
-    u32x4 hp, lp;
+  auto grads = [&](const TrOps &op, const bf16x8 (&x)[2]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float a = s[8 * t + 2 * j], b = s[8 * t + 2 * j + 1];
-      const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
-      hp[j] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
-      const bf16x2 r = {(__bf16)(a - __uint_as_float(ua & 0xffff0000u)),
-                        (__bf16)(b - __uint_as_float(ub & 0xffff0000u))};
-      lp[j] = __builtin_bit_cast(uint32_t, r);
-    }
-    ph = __builtin_bit_cast(bf16x8, hp);
-    pl = __builtin_bit_cast(bf16x8, lp);
-  };
-  auto grads = [&](const bf16x8 (&ops)[2 * C::NDB], int d, const bf16x8 &ph,
-                   const bf16x8 &ds) {
-    dva[d] = mfma32(ops[d], ph, dva[d]);
-    dka[d] = mfma32(ops[C::NDB + d], ds, dka[d]);
-  };
-  auto grads_lo = [&](const bf16x8 (&ops)[2 * C::NDB], const bf16x8 &pl) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int d = 0; d < C::NDB; ++d) dva[d] = mfma32(ops[d], pl, dva[d]);
+      for (int d = 0; d < C::NDB; ++d) acc[d] = mfma32(op[t][d], x[t], acc[d]);
   };
 
-  auto pin = [](float x) {
-    asm volatile("" ::"v"(x));
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // One pipeline step for tile qt: S', dP' of tile qt in (sc, dpc); the S'/dP'
-  // operands (qa, ga, xv) of tile qt + 1 in registers.  LDS reads are spread over
-  // the MFMA phases so that every wave keeps its MFMAs busy while the LDS serves
-  // the reads of all four:
-  //   phase 1: S', dP' of tile qt + 1 (when NEXT) into (sn, dpn), one MFMA pair per
-  //            slice, with a transposed operand read of tile qt rows 0..15 and the
-  //            P / dS work of two (D = 128) elements per slice;
-  //   phase 2a: dV^T, dK^T of rows 0..15, one 32-column block per slice, with the
-  //            transposed operand reads of rows 16..31;
-  //   phase 2b: dV^T, dK^T of rows 16..31, with the S'/dP' operand reads of tile
-  //            qt + 2 (when LOAD) for the next step.
-  // The tiles come in as distinct restrict pointers: the compiler then knows the
-  // reads do not touch the tile being copied and does not make them wait for the
-  // copies in flight (the tiles a step reads were awaited at an earlier barrier).
-  auto step_body = [&](auto mask_tag, auto next_tag, auto load_tag, int qt, f32x16 &sc,
-                       f32x16 &dpc, f32x16 &sn, f32x16 &dpn, bf16x8 (&qa)[C::KST],
-                       bf16x8 (&ga)[C::KST], float &xv, const uint16_t *__restrict__ cur,
-                       const uint16_t *__restrict__ nn, const float *__restrict__ vnn,
-                       uint16_t *__restrict__ dma, float *__restrict__ vdma)
-                       __attribute__((always_inline)) {
-    constexpr bool NEXT = decltype(next_tag)::value;
-    constexpr bool LOAD = decltype(load_tag)::value;
-    issue_to(qt + C::AHEAD, dma, vdma);
-    const int rel0 = qt * C::BQ + 8 * h - my_k;
-    bf16x8 op0[2 * C::NDB], op1[2 * C::NDB];
-    float pm = 0.f, dm = 0.f;
-    if constexpr (NEXT) {
-      const bf16x8 av = bcast_op(xv);
-      sn = mfma32(av, bsel_s, f32x16{});
-      dpn = mfma32(av, bsel_d, f32x16{});
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    constexpr int EPS = 16 / C::KST;  // elements per slice
+  // P side, tile qt: S', P (masked when MASK), P to the partner, dV^T += dO^T P.  P
+  // enters dV as bf16; where some P of the wave's tile reaches kLoP, it enters as hi +
+  // lo instead: hi = P truncated to bf16, lo = the exact remainder rounded to bf16
+  // (P = hi + lo to ~2^-16 relative).  A single bf16 P on those large values leaves
+  // |dV| >= 4 outside 2e-2 of the exact gradient; below kLoP the rounding of P
+  // (<= 2^-13 absolute) is far inside it.
+  auto p_side = [&](bool masked, int qt, const uint16_t *__restrict__ cur,
+                    const float *__restrict__ vt, float *__restrict__ xw)
+                    __attribute__((always_inline)) {
+    f32x16 s;
+    sdp(cur, vt, s);
+    TrOps op;
+    tr_ops(cur + C::TSZ, op);  // dO^T, read while P is formed
 #pragma unroll
-    for (int st = 0; st < C::KST; ++st) {
-      op0[st] = tr_op(cur, 0, st);
-      if constexpr (NEXT) {
-        sn = mfma32(qa[st], kr[st], sn);
-        dpn = mfma32(ga[st], vr[st], dpn);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      grad_elems(mask_tag, sc, dpc, pm, dm, rel0, EPS * st, EPS);
-      pin(dpc[EPS * st + EPS - 1]);
+    for (int i = 0; i < 16; ++i) s[i] = fast_exp2(s[i] * c);
+    // the element mask only changes P: the products below are the same code either way
+    if (masked) {
+      const int rel0 = qt * C::BQ + 8 * h - my_k;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        s[i] = (unsigned)(rel0 + 16 * (i >> 3) + (i & 7)) <= wm1 ? s[i] : 0.f;
     }
-    // phases 2a and 2b; the lo part of P only where the tile holds a large P, its
-    // MFMAs grouped after each phase (one branch per group)
+    float pm = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) pm = fmaxf(pm, fmaxf(s[i], s[i + 1]));
+    // the partner lane (same lane of wave w + 4) reads these 16 values
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4)
+      reinterpret_cast<f32x4 *>(xw)[64 * c4 + lane] =
+          f32x4{s[4 * c4], s[4 * c4 + 1], s[4 * c4 + 2], s[4 * c4 + 3]};
     const bool lo = __builtin_amdgcn_ballot_w64(pm >= kLoP) != 0;
-    const bool lods = kDsLoK<D> && __builtin_amdgcn_ballot_w64(dm >= kLoDsK) != 0;
-    bf16x8 ph0, pl0, ph1, pl1;
-    if (lo) {
-      pack_hilo(sc, 0, ph0, pl0);
-      pack_hilo(sc, 1, ph1, pl1);
-    } else {
-      ph0 = pack_rne(sc, 0);
-      ph1 = pack_rne(sc, 1);
+    bf16x8 ph[2];
+    if (lo) {  // hi = P truncated
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 hp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          hp[j] = __builtin_amdgcn_perm(__float_as_uint(s[8 * t + 2 * j + 1]),
+                                        __float_as_uint(s[8 * t + 2 * j]), 0x07060302u);
+        ph[t] = __builtin_bit_cast(bf16x8, hp);
+      }
+    } else {  // P rounded to nearest even
+#pragma unroll
+      for (int t = 0; t < 2; ++t) ph[t] = to_bf16x8(s, 8 * t);
     }
-    const bf16x8 ds0 = to_bf16x8(dpc, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    bf16x8 ds1;
+    grads(op, ph);
+    if (lo) {  // lo = the exact remainder P - hi, rounded
+      bf16x8 pl[2];
 #pragma unroll
-    for (int d = 0; d < C::NDB; ++d) {
-      op1[d] = tr_op(cur, 1, d);
-      op1[C::NDB + d] = tr_op(cur, 1, C::NDB + d);
-      grads(op0, d, ph0, ds0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (d == C::NDB - 1) ds1 = to_bf16x8(dpc, 8);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (lo) grads_lo(op0, pl0);
-    if (lods) grads_ds_lo(op0, pack_ds_lo(dpc, 0));
-    __builtin_amdgcn_sched_barrier(0);
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int d = 0; d < C::NDB; ++d) {
-      if constexpr (LOAD) {
-#pragma unroll
-        for (int u = 0; u < C::KST / C::NDB; ++u) {
-          const int st = (C::KST / C::NDB) * d + u;
-          qa[st] = read_q(nn, st);
-          ga[st] = read_q(nn + C::TSZ, st);
+        for (int j = 0; j < 8; ++j) {
+          const float a = s[8 * t + j];
+          pl[t][j] = (__bf16)(a - __uint_as_float(__float_as_uint(a) & 0xffff0000u));
         }
-        if (d == 0) xv = vnn[vrow];
+      grads(op, pl);
+    }
+  };
+  // dS side, tile qt - 1 (when DK): dS = P dP' with the partner's P, dK^T += Q^T dS; and
+  // tile qt (when DP): dP' into dpn.  dS enters dK as one bf16 unless some |dS| of the
+  // wave's tile reaches kLoDsK (D = 64): then also its remainder, rounded to bf16.
+  auto ds_side = [&](bool do_dk, bool do_dp, const uint16_t *__restrict__ cur,
+                     const float *__restrict__ vt, const uint16_t *__restrict__ prev,
+                     const float *__restrict__ xr, f32x16 &dpp, f32x16 &dpn)
+                     __attribute__((always_inline)) {
+    if (do_dk) {
+      TrOps op;
+      tr_ops(prev, op);  // Q^T of tile qt - 1
+      f32x16 p;
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const f32x4 x = reinterpret_cast<const f32x4 *>(xr)[64 * c4 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[4 * c4 + e] = x[e];
       }
-      grads(op1, d, ph1, ds1);
+      float dm = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dpp[i] = p[i] * dpp[i];
       __builtin_amdgcn_sched_barrier(0);
-    }
-    if (lo) grads_lo(op1, pl1);
-    if (lods) grads_ds_lo(op1, pack_ds_lo(dpc, 1));
-  };
-  auto step = [&](auto mask_tag, auto next_tag, auto load_tag, int qt, f32x16 &sc, f32x16 &dpc,
-                  f32x16 &sn, f32x16 &dpn, bf16x8 (&qa)[C::KST], bf16x8 (&ga)[C::KST],
-                  float &xv) __attribute__((always_inline)) {
-    step_body(mask_tag, next_tag, load_tag, qt, sc, dpc, sn, dpn, qa, ga, xv, q_tile(qt),
-              q_tile(qt + 2), vec_of(qt + 2), q_tile(qt + C::AHEAD), vec_of(qt + C::AHEAD));
-  };
-  // S', dP' of the wave's first tile t and the S'/dP' operands of tile t + 1.
-  auto pre_body = [&](int t, f32x16 &sc, f32x16 &dpc, bf16x8 (&qa)[C::KST],
-                      bf16x8 (&ga)[C::KST], float &xv, const uint16_t *__restrict__ t0p,
-                      const float *__restrict__ v0p, const uint16_t *__restrict__ t1p,
-                      const float *__restrict__ v1p) __attribute__((always_inline)) {
+      if constexpr (kDsLoK<D>) {
 #pragma unroll
-    for (int st = 0; st < C::KST; ++st) {
-      qa[st] = read_q(t0p, st);
-      ga[st] = read_q(t0p + C::TSZ, st);
-    }
-    xv = v0p[vrow];
-    sdp_from(qa, ga, xv, sc, dpc);
-    if (t + 1 <= wqt1) {
-#pragma unroll
-      for (int st = 0; st < C::KST; ++st) {
-        qa[st] = read_q(t1p, st);
-        ga[st] = read_q(t1p + C::TSZ, st);
+        for (int i = 0; i < 16; i += 2) dm = fmaxf(dm, fmaxf(fabsf(dpp[i]), fabsf(dpp[i + 1])));
       }
-      xv = v1p[vrow];
+      bf16x8 ds[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) ds[t] = to_bf16x8(dpp, 8 * t);
+      grads(op, ds);
+      if (kDsLoK<D> && __builtin_amdgcn_ballot_w64(dm >= kLoDsK) != 0) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            ds[t][j] = (__bf16)(dpp[8 * t + j] - (float)(__bf16)dpp[8 * t + j]);
+        grads(op, ds);
+      }
     }
-  };
-  // One barrier per two steps, after the steps qt with qt - qt0 odd: there, all
-  // copies but those of the last two steps (tiles qt + AHEAD - 1, qt + AHEAD) must
-  // have landed, so that the next two steps find tiles up to qt + 4 in LDS.  A step
-  // reads tiles qt .. qt + 2 and copies into the slot of tile qt - 2, both of them
-  // separated from the other uses of those slots by a barrier.  Every step issues
-  // its copies, also past the workgroup's last tile (rows from T on read as zero
-  // and land in slots no step reads), so the wait count is always the same.
-  auto sync = [&](int qt) {
-    if ((qt - qt0) & 1) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm<2 * C::NCOPY>);
-      lds_barrier();
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (do_dp) sdp(cur + C::TSZ, vt, dpn);
   };
 
-  // prologue: tiles qt0 .. qt0 + AHEAD - 1 in flight; those up to qt0 + 3 must land.
-  // The K / V row loads go between the copies of tiles qt0 + 3 and qt0 + 4, so all
-  // these memory latencies overlap and one wait covers the rows and the first four
-  // tiles (vector-memory operations complete in order).
-  for (int t = qt0; t < qt0 + 4; ++t) issue(t);
+  // Step qt: the copies of tile qt + AHEAD start (every step, also past the workgroup's
+  // last tile: rows from T on read as zero and land in a slot no step reads, and the
+  // wait count stays constant); the P side works on tile qt, the dS side on tiles
+  // qt - 1 (dK) and qt (dP).  At the end, the wave's copies of tile qt + 1 and all its
+  // LDS accesses are complete, then the barrier: tile qt + 1 and the P handed over in
+  // this step are visible to every wave, and the slot of tile qt - 1 (read in this
+  // step) is free for the copies of the next one.  The two roles run their own loops
+  // (so neither holds the other's registers) over the same steps and barriers.  The
+  // tiles and buffers come in as distinct restrict pointers, so the compiler does not
+  // make the reads wait for the copies in flight.
+  auto end_step = [&] {
+    __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0<C::NCOPY>);
+    lds_barrier();
+  };
+  auto p_step = [&](int qt, const uint16_t *__restrict__ cur, const float *__restrict__ vt,
+                    float *__restrict__ xw, uint16_t *__restrict__ dma,
+                    float *__restrict__ vdma) __attribute__((always_inline)) {
+    issue_to(qt + C::AHEAD, dma, vdma);
+    if (qt >= wqt0 && qt <= wqt1) p_side(qt == wqt0 || qt >= mlo, qt, cur, vt, xw);
+    end_step();
+  };
+  auto ds_step = [&](int qt, const uint16_t *__restrict__ cur, const float *__restrict__ vt,
+                     const uint16_t *__restrict__ prev, const float *__restrict__ xr,
+                     uint16_t *__restrict__ dma, float *__restrict__ vdma, f32x16 &dpp,
+                     f32x16 &dpn) __attribute__((always_inline)) {
+    issue_to(qt + C::AHEAD, dma, vdma);
+    ds_side(qt - 1 >= wqt0 && qt - 1 <= wqt1, qt >= wqt0 && qt <= wqt1, cur, vt, prev, xr, dpp,
+            dpn);
+    end_step();
+  };
+
+  // prologue: tiles qt0 and qt0 + 1 and the stationary rows, all awaited
+  issue(qt0);
+  issue(qt0 + 1);
   {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)T * rsk * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)T * rsk * 2);
+    const __amdgpu_buffer_rsrc_t rkv = make_rsrc(pside ? kb : vb, (uint32_t)T * rsk * 2);
 #pragma unroll
-    for (int st = 0; st < C::KST; ++st) {
-      const uint32_t off = (my_k * rsk + 16 * st + 8 * h) * 2;
-      kr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-      vr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
-    }
+    for (int st = 0; st < C::KST; ++st)
+      kv[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rkv, (my_k * rsk + 16 * st + 8 * h) * 2, 0, 0));
   }
-  static_assert(C::AHEAD == 6, "the prologue issues tiles qt0 + 4 and qt0 + 5 last");
-  issue(qt0 + 4);
-  issue(qt0 + 5);
-  __builtin_amdgcn_s_waitcnt(kWaitVm<2 * C::NCOPY>);
+  __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0<0>);
   lds_barrier();
 
-  f32x16 sa, dpa, sb, dpb;
-  bf16x8 qa[C::KST], ga[C::KST];
-  float xv = 0.f;
-  if (wqt0 == qt0)
-    pre_body(qt0, sa, dpa, qa, ga, xv, q_tile(qt0), vec_of(qt0), q_tile(qt0 + 1),
-             vec_of(qt0 + 1));
-
-  // Phases of the wave: idle tiles, the step before its first tile (S', dP' of that
-  // tile), its tiles (the first one and those from mlo on masked), idle tiles.  One
-  // barrier per tile of the workgroup in every phase.
-  using F = std::false_type;
-  using Tr = std::true_type;
-  int qt = qt0;
-  for (; qt < min(wqt0 - 1, qt1 + 1); ++qt) {
-    issue(qt + C::AHEAD);
-    sync(qt);
-  }
-  if (wqt0 > qt0 && qt == wqt0 - 1) {
-    issue(qt + C::AHEAD);
-    pre_body(qt + 1, sa, dpa, qa, ga, xv, q_tile(qt + 1), vec_of(qt + 1), q_tile(qt + 2),
-             vec_of(qt + 2));
-    sync(qt);
-    ++qt;
-  }
-  // The wave's tiles wqt0 .. wqt1; S' / dP' of tile qt in (sa, dpa) between steps.
-  // Step qt computes S' / dP' of tile qt + 1 when qt < wqt1 (NEXT) and reads the
-  // operands of tile qt + 2 when qt + 2 <= wqt1 (LOAD); tile wqt0, tiles from mlo on
-  // and the last two tiles run the element mask.
-  auto next = [&] {
-    sa = sb;
-    dpa = dpb;
-  };
-  if (qt == wqt0 && qt <= wqt1) {  // diagonal tile
-    if (qt + 2 <= wqt1) {
-      step(Tr{}, Tr{}, Tr{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
-      next();
-    } else if (qt + 1 <= wqt1) {
-      step(Tr{}, Tr{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
-      next();
-    } else {
-      step(Tr{}, F{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
+  // steps qt0 .. qt1 + 1 (the dS side's dK trails its dP by one step)
+  if (pside) {
+    for (int qt = qt0; qt <= qt1 + 1; ++qt)
+      p_step(qt, q_tile(qt), vec_of(qt), xp_of(qt), q_tile(qt + C::AHEAD),
+             vec_of(qt + C::AHEAD));
+  } else {
+    f32x16 dpa = f32x16{}, dpb = f32x16{};
+    int qt = qt0;
+    // two steps per iteration: dP' alternates between dpa and dpb
+    for (; qt + 1 <= qt1 + 1; qt += 2) {
+      ds_step(qt, q_tile(qt), vec_of(qt), q_tile(qt - 1), xp_of(qt - 1), q_tile(qt + C::AHEAD),
+              vec_of(qt + C::AHEAD), dpa, dpb);
+      ds_step(qt + 1, q_tile(qt + 1), vec_of(qt + 1), q_tile(qt), xp_of(qt),
+              q_tile(qt + 1 + C::AHEAD), vec_of(qt + 1 + C::AHEAD), dpb, dpa);
     }
-    sync(qt);
-    ++qt;
-  }
-  // unmasked steps with NEXT and LOAD, two per iteration (no register copies)
-  const int ulim = min(wqt1 - 1, mlo);
-  for (; qt + 1 < ulim; qt += 2) {
-    step(F{}, Tr{}, Tr{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
-    sync(qt);
-    step(F{}, Tr{}, Tr{}, qt + 1, sb, dpb, sa, dpa, qa, ga, xv);
-    sync(qt + 1);
-  }
-  if (qt < ulim) {
-    step(F{}, Tr{}, Tr{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
-    next();
-    sync(qt);
-    ++qt;
-  }
-  // masked steps with NEXT and LOAD
-  for (; qt < wqt1 - 1; ++qt) {
-    step(Tr{}, Tr{}, Tr{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
-    next();
-    sync(qt);
-  }
-  // the last two steps always run the element mask (it keeps every element of an
-  // unmasked tile): one code path each
-  if (qt == wqt1 - 1) {
-    step(Tr{}, Tr{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
-    next();
-    sync(qt);
-    ++qt;
-  }
-  if (qt == wqt1) {
-    step(Tr{}, F{}, F{}, qt, sa, dpa, sb, dpb, qa, ga, xv);
-    sync(qt);
-    ++qt;
-  }
-  for (; qt <= qt1; ++qt) {
-    issue(qt + C::AHEAD);
-    sync(qt);
+    if (qt == qt1 + 1)
+      ds_step(qt, q_tile(qt), vec_of(qt), q_tile(qt - 1), xp_of(qt - 1), q_tile(qt + C::AHEAD),
+              vec_of(qt + C::AHEAD), dpa, dpb);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm<0>);  // no copy into LDS outlives the workgroup
 
-  if (PARTIAL) {
-    if (my_k < T) {
-      float *pk = part_k + base + (size_t)my_k * rs, *pv = part_v + base + (size_t)my_k * rs;
+  if (my_k < T) {
+    if (PARTIAL) {
+      float *pp = (pside ? part_v : part_k) + base + (size_t)my_k * rs;
+      const float mul = pside ? 1.f : scale;
 #pragma unroll
       for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          f32x4 a, c4;
+          f32x4 a;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a[e] = dka[d][4 * g + e] * scale;
-            c4[e] = dva[d][4 * g + e];
-          }
-          *reinterpret_cast<f32x4 *>(pk + 32 * d + 8 * g + 4 * h) = a;
-          *reinterpret_cast<f32x4 *>(pv + 32 * d + 8 * g + 4 * h) = c4;
+          for (int e = 0; e < 4; ++e) a[e] = acc[d][4 * g + e] * mul;
+          *reinterpret_cast<f32x4 *>(pp + 32 * d + 8 * g + 4 * h) = a;
+        }
+    } else {
+      uint16_t *ob = (pside ? dv : dk) + base_kv + (size_t)my_k * rsk;
+      const float mul = pside ? 1.f : scale;
+#pragma unroll
+      for (int d = 0; d < C::NDB; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[d][4 * g + e] * mul);
+          *reinterpret_cast<bf16x4 *>(ob + 32 * d + 8 * g + 4 * h) = pk;
         }
     }
-  } else if (my_k < T) {
-    uint16_t *dkb = dk + base_kv + (size_t)my_k * rsk, *dvb = dv + base_kv + (size_t)my_k * rsk;
-#pragma unroll
-    for (int d = 0; d < C::NDB; ++d)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 pk, pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pk[e] = (__bf16)(dka[d][4 * g + e] * scale);
-          pv[e] = (__bf16)dva[d][4 * g + e];
-        }
-        *reinterpret_cast<bf16x4 *>(dkb + 32 * d + 8 * g + 4 * h) = pk;
-        *reinterpret_cast<bf16x4 *>(dvb + 32 * d + 8 * g + 4 * h) = pv;
-      }
   }
 }
 
@@ -582,7 +460,7 @@ static void launch_dkdv_t(const void *q, const void *k, const void *v, const voi
                           float scale, hipStream_t st) {
   const int nkt = (T + DkdvCfg<D>::BK - 1) / DkdvCfg<D>::BK;
   const unsigned nb = (unsigned)(nkt * B * H);
-  bwd_dkdv_bf16_kernel<D, PARTIAL><<<nb, 256, 0, st>>>(
+  bwd_dkdv_bf16_kernel<D, PARTIAL><<<nb, DkdvCfg<D>::NW * 64, 0, st>>>(
       (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dO, lse,
       delta, (uint16_t *)dk, (uint16_t *)dv, part_k, part_v, B, H, Hkv, T, window, scale, nkt);
 }
