@@ -381,6 +381,71 @@ def bench_prologue(torch, swattn, inputs, iters, cfg_name="small"):
     return res
 
 
+def bench_rope_step(torch, swattn, inputs, steps, warmup, ramp_s):
+    """A training step through the QK-norm + rotary prologue and attention on the small
+    workload's shape (raw q, k projections), two ways:
+      unfused: two-sided prologue, swattn_fwd, swattn_bwd, prologue backward;
+      fused:   keys-only prologue, swattn_fwd_rope (writes q'), swattn_bwd_rope.
+    Both timed like the headline (ramp, warm-up, one timed region).  Algorithmic bytes
+    of the prologue part: unfused 4 + 6 tensors of q's size (read q, k, write q', k';
+    read q, k, dq', dk', write dq, dk); fused 2 (read k, write k') + 1 (the forward
+    writes q') + 2 (the dQ and dK/dV epilogues read q and k again)."""
+    c = inputs.CONFIGS["small"]
+    B, H, T, D = c["B"], c["H"], c["T"], c["D"]
+    scale = 1.0 / math.sqrt(D)
+    x = inputs.training_inputs(B, T, H, D, "bf16", c["seeds"][0], qk_norm=False)
+    g = {n: t.to("cuda:0") for n, t in x.items()}
+    e = lambda: torch.empty_like(g["q"])  # noqa: E731
+    yq, yk, o, dyq, dyk, dq, dk, dv, kr, qr = (e() for _ in range(10))
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(swattn.swattn_bwd_workspace_size(B, H, T, D), dtype=torch.uint8,
+                     device="cuda:0")
+    lib, P = swattn.lib(), swattn._ptr
+    sh = swattn.ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    base, eps = 10000.0, 1e-6
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"rope step: status {rc}")
+
+    def unfused():
+        ok(lib.swattn_qk_norm_rope(P(g["q"]), P(g["k"]), P(yq), P(yk), None, B, T, H, H, D, base,
+                                   eps, sh))
+        ok(lib.swattn_fwd(P(yq), P(yk), P(g["v"]), P(o), P(lse), B, H, T, D, -1, scale, sh))
+        ok(lib.swattn_bwd(P(yq), P(yk), P(g["v"]), P(o), P(g["do"]), P(lse), P(dyq), P(dyk), P(dv),
+                          B, H, T, D, -1, scale, P(ws), sh))
+        ok(lib.swattn_qk_norm_rope_bwd(P(g["q"]), P(g["k"]), P(dyq), P(dyk), P(dq), P(dk), None, B,
+                                       T, H, H, D, base, eps, sh))
+
+    def fused():
+        ok(lib.swattn_qk_norm_rope(None, P(g["k"]), None, P(kr), None, B, T, 0, H, D, base, eps,
+                                   sh))
+        ok(lib.swattn_fwd_rope(P(g["q"]), P(kr), P(g["v"]), P(o), P(lse), P(qr), None, B, H, T, D,
+                               -1, scale, base, eps, sh))
+        ok(lib.swattn_bwd_rope(P(g["q"]), P(g["k"]), P(qr), P(kr), P(g["v"]), P(o), P(g["do"]),
+                               P(lse), P(dq), P(dk), P(dv), None, B, H, T, D, -1, scale, base, eps,
+                               P(ws), sh))
+
+    out = {"workload": f"small: B{B} H{H} T{T} D{D} bf16, raw q and k, full causal; "
+                       f"prologue + attention forward + backward"}
+    t_bytes = B * T * H * D * 2
+    for name, fn, nb in (("unfused", unfused, 10 * t_bytes), ("fused", fused, 5 * t_bytes)):
+        clock_ramp(torch, fn, ramp_s)
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        out[name] = {"ms_per_step": round(ms, 4), "prologue_bytes": nb}
+    out["saved_us_per_step"] = round((out["unfused"]["ms_per_step"] - out["fused"]["ms_per_step"])
+                                     * 1e3, 1)
+    out["saved_bytes_per_step"] = out["unfused"]["prologue_bytes"] - out["fused"]["prologue_bytes"]
+    return out
+
+
 def bench_prefill(torch, swattn, inputs, iters, tq=512):
     """Chunked prefill on the decode workload's caches: each of the 32 sequences appends a
     chunk of ``tq`` tokens at (its decode length - tq) and attends the chunk's queries to
@@ -807,6 +872,9 @@ def main():
         log(f"prefill {res['prefill']}")
         res["qk_prologue"] = bench_prologue(torch, swattn, inputs, args.decode_iters)
         log(f"qk prologue {res['qk_prologue']}")
+        res["qk_rope_step"] = bench_rope_step(torch, swattn, inputs, args.steps, args.warmup,
+                                              args.ramp_s / 4)
+        log(f"qk rope step {res['qk_rope_step']}")
     if args.hkv:
         res["training_gqa"] = bench_training_gqa(torch, swattn, inputs, args.config, args.hkv,
                                                  max(50, args.steps // 4), max(50, args.warmup // 2))

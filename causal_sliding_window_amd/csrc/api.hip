@@ -366,7 +366,9 @@ int swattn_decode_f32(const float *q, const float *k_cache, const float *v_cache
 }
 
 static int check_prologue(int B, int T, int H, int Hkv, int D, float base, float eps) {
-  if (B <= 0 || T <= 0 || H <= 0 || Hkv <= 0 || D <= 0) return SWATTN_ERR_INVALID_ARG;
+  // H == 0 (keys only) or Hkv == 0 (queries only) is allowed, not both
+  if (B <= 0 || T <= 0 || H < 0 || Hkv < 0 || H + Hkv == 0 || D <= 0)
+    return SWATTN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return SWATTN_ERR_UNSUPPORTED;
   if (!(base > 0.f) || !std::isfinite(base) || !(eps >= 0.f) || !std::isfinite(eps))
     return SWATTN_ERR_INVALID_ARG;
@@ -379,7 +381,8 @@ int swattn_qk_norm_rope(const void *q, const void *k, void *q_out, void *k_out,
                         float eps, swattn_stream_t stream) {
   const int st = check_prologue(B, T, H, Hkv, D, base, eps);
   if (st != SWATTN_OK) return st;
-  if (!all_aligned({q, k, q_out, k_out})) return SWATTN_ERR_INVALID_ARG;
+  if ((H > 0 && !all_aligned({q, q_out})) || (Hkv > 0 && !all_aligned({k, k_out})))
+    return SWATTN_ERR_INVALID_ARG;
   return hip_status(swattn::launch_qk_norm_rope(q, k, q_out, k_out, pos_offset, B, T, H, Hkv, D,
                                                 base, eps, (hipStream_t)stream));
 }
@@ -390,10 +393,62 @@ int swattn_qk_norm_rope_bwd(const void *q, const void *k, const void *dq_out,
                             swattn_stream_t stream) {
   const int st = check_prologue(B, T, H, Hkv, D, base, eps);
   if (st != SWATTN_OK) return st;
-  if (!all_aligned({q, k, dq_out, dk_out, dq, dk})) return SWATTN_ERR_INVALID_ARG;
+  if ((H > 0 && !all_aligned({q, dq_out, dq})) || (Hkv > 0 && !all_aligned({k, dk_out, dk})))
+    return SWATTN_ERR_INVALID_ARG;
   return hip_status(swattn::launch_qk_norm_rope_bwd(q, k, dq_out, dk_out, dq, dk, pos_offset, B,
                                                     T, H, Hkv, D, base, eps,
                                                     (hipStream_t)stream));
+}
+
+static int check_rope_args(float base, float eps) {
+  if (!(base > 0.f) || !std::isfinite(base) || !(eps >= 0.f) || !std::isfinite(eps))
+    return SWATTN_ERR_INVALID_ARG;
+  return SWATTN_OK;
+}
+
+static swattn::RopeArgs rope_args(const int *pos_offset, int D, float base, float eps) {
+  swattn::RopeArgs ra;
+  ra.pos_off = pos_offset;
+  ra.ratio = std::pow((double)base, -2.0 / D);
+  ra.eps = eps;
+  return ra;
+}
+
+int swattn_fwd_rope(const void *q, const void *k_rope, const void *v, void *o, float *lse,
+                    void *q_rope, const int *pos_offset, int B, int H, int T, int D, int window,
+                    float scale, float base, float eps, swattn_stream_t stream) {
+  int st = check_common(B, H, T, D, window);
+  if (st == SWATTN_OK) st = check_scale(scale);
+  if (st == SWATTN_OK) st = check_rope_args(base, eps);
+  if (st != SWATTN_OK) return st;
+  if (!all_aligned({q, k_rope, v, o}) || lse == nullptr) return SWATTN_ERR_INVALID_ARG;
+  if (q_rope != nullptr && !all_aligned({q_rope})) return SWATTN_ERR_INVALID_ARG;
+  const swattn::RopeArgs ra = rope_args(pos_offset, D, base, eps);
+  return hip_status(swattn::launch_fwd_bf16_rope(q, k_rope, v, o, lse, q_rope, B, H, T, D, window,
+                                                 scale, ra, (hipStream_t)stream));
+}
+
+int swattn_bwd_rope(const void *q, const void *k, const void *q_rope, const void *k_rope,
+                    const void *v, const void *o, const void *dO, const float *lse, void *dq,
+                    void *dk, void *dv, const int *pos_offset, int B, int H, int T, int D,
+                    int window, float scale, float base, float eps, void *workspace,
+                    swattn_stream_t stream) {
+  int s = check_common(B, H, T, D, window);
+  if (s == SWATTN_OK) s = check_scale(scale);
+  if (s == SWATTN_OK) s = check_rope_args(base, eps);
+  if (s != SWATTN_OK) return s;
+  if (!all_aligned({q, k, q_rope, k_rope, v, o, dO, dq, dk, dv, workspace}) || lse == nullptr)
+    return SWATTN_ERR_INVALID_ARG;
+  const swattn::RopeArgs ra = rope_args(pos_offset, D, base, eps);
+  float *delta = (float *)workspace;
+  // dQ pass: raw q held (and transformed) in registers, transformed k streamed; dK/dV pass:
+  // raw k held, transformed q streamed
+  hipError_t e = swattn::launch_bwd_dq_bf16(q, k_rope, v, o, dO, lse, delta, dq, B, H, H, T, D,
+                                             window, scale, (hipStream_t)stream, &ra);
+  if (e == hipSuccess)
+    e = swattn::launch_bwd_dkdv_bf16(q_rope, k, v, dO, lse, delta, dk, dv, nullptr, B, H, H, T, D,
+                                     window, scale, (hipStream_t)stream, &ra);
+  return hip_status(e);
 }
 
 }  // extern "C"

@@ -20,6 +20,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "rope.h"
 
 namespace swattn {
 
@@ -73,12 +74,16 @@ constexpr float kLoDs = 1.0f;
 template <int D>
 constexpr bool kDsLo = D == 64;
 
-template <int D>
+// ROPE: q holds the raw queries (k the transformed keys); each query is normalised and
+// rotated (QK norm + rotary embedding) as it is loaded, and dq is the gradient with
+// respect to the raw query: the epilogue maps dL/dq' back through the prologue.
+template <int D, bool ROPE = false>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ o,
     const uint16_t *__restrict__ dO, const float *__restrict__ lse, float *__restrict__ delta,
-    uint16_t *__restrict__ dq, int B, int H, int Hkv, int T, int window, float scale, int nqt) {
+    uint16_t *__restrict__ dq, int B, int H, int Hkv, int T, int window, float scale, int nqt,
+    RopeArgs ra = RopeArgs{}) {
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::NSLOT * 2 * C::TSZ];  // [slot][K, V]
 
@@ -124,6 +129,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     qr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     gr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
   }
+  if constexpr (ROPE) rope_norm_operand<D>(qr, rope_pos(ra, b, my_q), my_q < T, ra, h);
   const float l2 = my_q < T ? lse[(size_t)bh * T + my_q] * kLog2e : INFINITY;
   // delta = dO . o of the lane's query (each half of the wave holds half of the
   // row), also published in the workspace for the dK/dV pass
@@ -365,6 +371,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm<0>);  // no copy into LDS outlives the workgroup
 
+#pragma unroll
+  for (int d = 0; d < C::NDB; ++d) acc[d] *= scale;  // dL/dq (dL/dq' with ROPE)
+  if constexpr (ROPE) {
+    // back through the prologue, with the raw query row read again (every lane of the
+    // wave takes part: the reductions pair lanes l and l ^ 32)
+    // (the query index and the frequency ratio made opaque, so that nothing of the load's
+    // prologue is held in registers through the loop for this)
+    int qi = my_q;
+    RopeArgs re = ra;
+    asm volatile("" : "+v"(qi), "+s"(re.ratio));
+    f32x16 xr[C::NDB];
+    load_acc_order<D>(qb + (size_t)min(qi, T - 1) * rs, h, xr);
+    rope_norm_grad_acc<D>(acc, xr, rope_pos(re, b, qi), qi < T, re, h);
+  }
   if (my_q < T) {
     uint16_t *dqr = dq + base + (size_t)my_q * rs;
 #pragma unroll
@@ -373,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
       for (int g = 0; g < 4; ++g) {
         bf16x4 pk;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[d][4 * g + e] * scale);
+        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)acc[d][4 * g + e];
         *reinterpret_cast<bf16x4 *>(dqr + 32 * d + 8 * g + 4 * h) = pk;
       }
   }
@@ -393,20 +413,33 @@ hipError_t launch_bwd_pre_bf16(const void *o, const void *dO, float *delta, int 
   return hipGetLastError();
 }
 
+template <int D, bool ROPE>
+static void launch_dq_t(const void *q, const void *k, const void *v, const void *o, const void *dO,
+                        const float *lse, float *delta, void *dq, int B, int H, int Hkv, int T,
+                        int window, float scale, const RopeArgs &ra, hipStream_t st) {
+  const int nqt = (T + 127) / 128;
+  const unsigned nb = (unsigned)(nqt * B * H);
+  bwd_dq_bf16_kernel<D, ROPE><<<nb, 256, 0, st>>>(
+      (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)o,
+      (const uint16_t *)dO, lse, delta, (uint16_t *)dq, B, H, Hkv, T, window, scale, nqt, ra);
+}
+
 hipError_t launch_bwd_dq_bf16(const void *q, const void *k, const void *v, const void *o,
                               const void *dO, const float *lse, float *delta, void *dq, int B,
                               int H, int Hkv, int T, int D, int window, float scale,
-                              hipStream_t st) {
-  const int nqt = (T + 127) / 128;
-  const unsigned nb = (unsigned)(nqt * B * H);
-  if (D == 128)
-    bwd_dq_bf16_kernel<128><<<nb, 256, 0, st>>>(
-        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)o,
-        (const uint16_t *)dO, lse, delta, (uint16_t *)dq, B, H, Hkv, T, window, scale, nqt);
-  else
-    bwd_dq_bf16_kernel<64><<<nb, 256, 0, st>>>(
-        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)o,
-        (const uint16_t *)dO, lse, delta, (uint16_t *)dq, B, H, Hkv, T, window, scale, nqt);
+                              hipStream_t st, const RopeArgs *rope) {
+  if (rope != nullptr) {
+    if (D == 128)
+      launch_dq_t<128, true>(q, k, v, o, dO, lse, delta, dq, B, H, Hkv, T, window, scale, *rope, st);
+    else
+      launch_dq_t<64, true>(q, k, v, o, dO, lse, delta, dq, B, H, Hkv, T, window, scale, *rope, st);
+  } else if (D == 128) {
+    launch_dq_t<128, false>(q, k, v, o, dO, lse, delta, dq, B, H, Hkv, T, window, scale,
+                            RopeArgs{}, st);
+  } else {
+    launch_dq_t<64, false>(q, k, v, o, dO, lse, delta, dq, B, H, Hkv, T, window, scale,
+                           RopeArgs{}, st);
+  }
   return hipGetLastError();
 }
 

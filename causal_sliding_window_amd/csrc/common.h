@@ -66,6 +66,14 @@ __device__ __forceinline__ bf16x8 to_bf16x8(f32x16 s, int base) {
   return r;
 }
 
+// Eight fp32 -> bf16 (round to nearest even) from an array.
+__device__ __forceinline__ bf16x8 to_bf16x8_arr(const float (&f)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (__bf16)f[j];
+  return r;
+}
+
 __device__ __forceinline__ bf16x8 lds_read_b128(const uint16_t *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }

@@ -19,6 +19,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "rope.h"
 
 namespace swattn {
 
@@ -71,13 +72,18 @@ constexpr int kWaitVmLgkm0 = (N & 15) | ((N >> 4) << 14) | (7 << 4);
 // the G = H / Hkv that read K/V head h / G; it writes its fp32 contributions to dK
 // (already scaled) and dV to part_k / part_v, [B, T, H, D], and dkdv_group_sum_kernel
 // adds the G of each K/V head.  Otherwise dk and dv are written directly.
-template <int D, bool PARTIAL>
+// ROPE (no K/V head groups): k holds the raw keys (q the transformed queries); each key
+// row is normalised and rotated (QK norm + rotary embedding) as the P side loads it, and
+// dk is the gradient with respect to the raw key: the dS side's epilogue maps dL/dk'
+// back through the prologue.
+template <int D, bool PARTIAL, bool ROPE = false>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, uint16_t *__restrict__ dk,
     uint16_t *__restrict__ dv, float *__restrict__ part_k, float *__restrict__ part_v, int B,
-    int H, int Hkv, int T, int window, float scale, int nkt) {
+    int H, int Hkv, int T, int window, float scale, int nkt, RopeArgs ra = RopeArgs{}) {
+  static_assert(!(ROPE && PARTIAL), "the fused prologue serves H == Hkv only");
   using C = DkdvCfg<D>;
   // One LDS array (with a single __shared__ variable the compiler keeps the restrict
   // scopes below): [slot][Q, dO][TSZ] bf16, then [slot][VSZ] float (lse, delta,
@@ -359,6 +365,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
                                               rkv, (my_k * rsk + 16 * st + 8 * h) * 2, 0, 0));
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0<0>);
+  if constexpr (ROPE) {
+    if (pside) rope_norm_operand<D>(kv, rope_pos(ra, b, my_k), my_k < T, ra, h);
+  }
   lds_barrier();
 
   // steps qt0 .. qt1 + 1 (the dS side's dK trails its dP by one step)
@@ -382,6 +391,35 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm<0>);  // no copy into LDS outlives the workgroup
 
+  if constexpr (ROPE) {
+    if (!pside) {
+      // dk: back through the prologue, with the raw key row read again (every lane of
+      // the wave takes part: the reductions pair lanes l and l ^ 32); the key index and
+      // the frequency ratio made opaque, so that nothing of the P side's prologue is
+      // held in registers through the loop for this
+      int ki = my_k;
+      RopeArgs re = ra;
+      asm volatile("" : "+v"(ki), "+s"(re.ratio));
+#pragma unroll
+      for (int d = 0; d < C::NDB; ++d) acc[d] *= scale;
+      f32x16 xr[C::NDB];
+      load_acc_order<D>(kb + (size_t)min(ki, T - 1) * rsk, h, xr);
+      rope_norm_grad_acc<D>(acc, xr, rope_pos(re, b, ki), ki < T, re, h);
+      if (ki < T) {
+        uint16_t *ob = dk + base_kv + (size_t)ki * rsk;
+#pragma unroll
+        for (int d = 0; d < C::NDB; ++d)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x4 pk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pk[e] = (__bf16)acc[d][4 * g + e];
+            *reinterpret_cast<bf16x4 *>(ob + 32 * d + 8 * g + 4 * h) = pk;
+          }
+      }
+      return;
+    }
+  }
   if (my_k < T) {
     if (PARTIAL) {
       float *pp = (pside ? part_v : part_k) + base + (size_t)my_k * rs;
@@ -453,22 +491,32 @@ __global__ __launch_bounds__(256) void dkdv_group_sum_kernel(const float *__rest
   *reinterpret_cast<bf16x4 *>(dv + e + 4) = b1;
 }
 
-template <int D, bool PARTIAL>
+template <int D, bool PARTIAL, bool ROPE = false>
 static void launch_dkdv_t(const void *q, const void *k, const void *v, const void *dO,
                           const float *lse, const float *delta, void *dk, void *dv,
                           float *part_k, float *part_v, int B, int H, int Hkv, int T, int window,
-                          float scale, hipStream_t st) {
+                          float scale, hipStream_t st, const RopeArgs &ra = RopeArgs{}) {
   const int nkt = (T + DkdvCfg<D>::BK - 1) / DkdvCfg<D>::BK;
   const unsigned nb = (unsigned)(nkt * B * H);
-  bwd_dkdv_bf16_kernel<D, PARTIAL><<<nb, DkdvCfg<D>::NW * 64, 0, st>>>(
+  bwd_dkdv_bf16_kernel<D, PARTIAL, ROPE><<<nb, DkdvCfg<D>::NW * 64, 0, st>>>(
       (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dO, lse,
-      delta, (uint16_t *)dk, (uint16_t *)dv, part_k, part_v, B, H, Hkv, T, window, scale, nkt);
+      delta, (uint16_t *)dk, (uint16_t *)dv, part_k, part_v, B, H, Hkv, T, window, scale, nkt, ra);
 }
 
 hipError_t launch_bwd_dkdv_bf16(const void *q, const void *k, const void *v, const void *dO,
                                 const float *lse, const float *delta, void *dk, void *dv,
                                 float *part, int B, int H, int Hkv, int T, int D, int window,
-                                float scale, hipStream_t st) {
+                                float scale, hipStream_t st, const RopeArgs *rope) {
+  if (rope != nullptr) {
+    if (Hkv != H) return hipErrorInvalidValue;  // the fused prologue serves H == Hkv only
+    if (D == 128)
+      launch_dkdv_t<128, false, true>(q, k, v, dO, lse, delta, dk, dv, nullptr, nullptr, B, H, H,
+                                      T, window, scale, st, *rope);
+    else
+      launch_dkdv_t<64, false, true>(q, k, v, dO, lse, delta, dk, dv, nullptr, nullptr, B, H, H,
+                                     T, window, scale, st, *rope);
+    return hipGetLastError();
+  }
   if (Hkv == H) {
     if (D == 128)
       launch_dkdv_t<128, false>(q, k, v, dO, lse, delta, dk, dv, nullptr, nullptr, B, H, Hkv, T,

@@ -35,6 +35,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "rope.h"
 
 namespace swattn {
 
@@ -56,12 +57,14 @@ constexpr int kPrefillOrderMaxB = 256;
 // Row-max growth (exp2 units) tolerated before the running max is moved.
 constexpr float kRescaleLog2 = 8.f;
 
-template <int D, bool PREFILL>
+// ROPE: q holds the raw queries; each is normalised and rotated (QK norm + rotary
+// embedding) as it is loaded into registers, and written to q_rope when that is not null.
+template <int D, bool PREFILL, bool ROPE = false>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
     const int *__restrict__ seqlens, int B, int H, int Hkv, int T, int Tkv, int window,
-    float scale, int nqt) {
+    float scale, int nqt, RopeArgs ra = RopeArgs{}, uint16_t *__restrict__ q_rope = nullptr) {
   using C = FwdCfg<D>;
   // [slot][K, V][TSZ]
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * C::TSZ];
@@ -136,6 +139,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       qr[st] = __builtin_bit_cast(
           bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, ((my_q - off) * rs + 16 * st + 8 * h) * 2,
                                                         0, 0));
+  }
+  if constexpr (ROPE) {
+    rope_norm_operand<D>(qr, rope_pos(ra, b, my_q - off), my_q < Tk, ra, h);
+    if (q_rope != nullptr && my_q < Tk) {
+      uint16_t *qo = q_rope + base + (size_t)(my_q - off) * rs + 8 * h;
+#pragma unroll
+      for (int st = 0; st < C::KST; ++st) *reinterpret_cast<bf16x8 *>(qo + 16 * st) = qr[st];
+    }
   }
 
   // Copy j of a tile (1 KB): LDS block db = j / RG, rows 16 (j % RG) .. + 15.
@@ -433,6 +444,22 @@ hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o,
     fwd_bf16_kernel<64, false><<<grid, block, 0, st>>>(
         (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr,
         B, H, Hkv, T, T, window, scale, nqt);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16_rope(const void *q, const void *k, const void *v, void *o, float *lse,
+                                void *q_rope, int B, int H, int T, int D, int window, float scale,
+                                const RopeArgs &ra, hipStream_t st) {
+  const int nqt = (T + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
+  dim3 grid((unsigned)(nqt * B * H)), block(256);
+  if (D == 128)
+    fwd_bf16_kernel<128, false, true><<<grid, block, 0, st>>>(
+        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr,
+        B, H, H, T, T, window, scale, nqt, ra, (uint16_t *)q_rope);
+  else
+    fwd_bf16_kernel<64, false, true><<<grid, block, 0, st>>>(
+        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr,
+        B, H, H, T, T, window, scale, nqt, ra, (uint16_t *)q_rope);
   return hipGetLastError();
 }
 

@@ -53,6 +53,8 @@ _SIGS = {
     "swattn_prefill": ([_P] * 8 + [_I] * 7 + [_F, _P], _I),
     "swattn_qk_norm_rope": ([_P] * 5 + [_I] * 5 + [_F, _F, _P], _I),
     "swattn_qk_norm_rope_bwd": ([_P] * 7 + [_I] * 5 + [_F, _F, _P], _I),
+    "swattn_fwd_rope": ([_P] * 7 + [_I] * 5 + [_F, _F, _F, _P], _I),
+    "swattn_bwd_rope": ([_P] * 12 + [_I] * 5 + [_F, _F, _F, _P, _P], _I),
 }
 
 
@@ -336,11 +338,20 @@ def swattn_prefill(q, k_new, v_new, k_cache, v_cache, seqlens, o, lse, window: i
 
 
 def _prologue_shapes(q, k, pos_offset, tensors):
-    B, T, H, D = q.shape
-    Hkv = k.shape[2]
+    """Shapes of a prologue call; q or k may be None (that side absent: H or Hkv = 0)."""
+    ref = q if q is not None else k
+    if ref is None:
+        raise SwattnError("the prologue needs q or k")
+    B, T, _, D = ref.shape
+    H = 0 if q is None else q.shape[2]
+    Hkv = 0 if k is None else k.shape[2]
     for n, t in tensors:
-        _dev_tensor(t, n, torch.bfloat16, (B, T, H, D) if n.startswith(("q", "dq")) else
-                    (B, T, Hkv, D))
+        is_q = n.startswith(("q", "dq"))
+        if (H if is_q else Hkv) == 0:
+            if t is not None:
+                raise SwattnError(f"{n} given for an absent side")
+            continue
+        _dev_tensor(t, n, torch.bfloat16, (B, T, H, D) if is_q else (B, T, Hkv, D))
     if pos_offset is not None:
         _dev_tensor(pos_offset, "pos_offset", torch.int32, (B,))
     return B, T, H, Hkv, D
@@ -354,7 +365,8 @@ def swattn_qk_norm_rope(q, k, q_out, k_out, pos_offset=None, base: float = 10000
                                                           ("k_out", k_out)))
     _check(lib().swattn_qk_norm_rope(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(pos_offset),
                                      B, T, H, Hkv, D, float(base), float(eps),
-                                     _stream(stream, q.device)), "swattn_qk_norm_rope")
+                                     _stream(stream, (q if q is not None else k).device)),
+           "swattn_qk_norm_rope")
 
 
 def swattn_qk_norm_rope_bwd(q, k, dq_out, dk_out, dq, dk, pos_offset=None,
@@ -364,8 +376,49 @@ def swattn_qk_norm_rope_bwd(q, k, dq_out, dk_out, dq, dk, pos_offset=None,
         ("q", q), ("k", k), ("dq_out", dq_out), ("dk_out", dk_out), ("dq", dq), ("dk", dk)))
     _check(lib().swattn_qk_norm_rope_bwd(_ptr(q), _ptr(k), _ptr(dq_out), _ptr(dk_out), _ptr(dq),
                                          _ptr(dk), _ptr(pos_offset), B, T, H, Hkv, D, float(base),
-                                         float(eps), _stream(stream, q.device)),
+                                         float(eps),
+                                         _stream(stream, (q if q is not None else k).device)),
            "swattn_qk_norm_rope_bwd")
+
+
+def swattn_fwd_rope(q, k_rope, v, o, lse, q_rope, window: int, scale: float, pos_offset=None,
+                    base: float = 10000.0, eps: float = 1e-6, stream=None):
+    """Forward with the QK-norm + rotary prologue fused into the query load (bf16, H == Hkv):
+    raw q, transformed k_rope; q_rope (or None) receives the transformed queries."""
+    B, T, H, D = q.shape
+    for n, t in (("q", q), ("k_rope", k_rope), ("v", v), ("o", o)):
+        _dev_tensor(t, n, torch.bfloat16, (B, T, H, D))
+    if q_rope is not None:
+        _dev_tensor(q_rope, "q_rope", torch.bfloat16, (B, T, H, D))
+    _dev_tensor(lse, "lse", torch.float32, (B, H, T))
+    if pos_offset is not None:
+        _dev_tensor(pos_offset, "pos_offset", torch.int32, (B,))
+    _check(lib().swattn_fwd_rope(_ptr(q), _ptr(k_rope), _ptr(v), _ptr(o), _ptr(lse), _ptr(q_rope),
+                                 _ptr(pos_offset), B, H, T, D, int(window), float(scale),
+                                 float(base), float(eps), _stream(stream, q.device)),
+           "swattn_fwd_rope")
+
+
+def swattn_bwd_rope(q, k, q_rope, k_rope, v, o, do, lse, dq, dk, dv, window: int, scale: float,
+                    workspace, pos_offset=None, base: float = 10000.0, eps: float = 1e-6,
+                    stream=None):
+    """Backward through attention and the fused prologue (bf16, H == Hkv): dq, dk with
+    respect to the raw q, k."""
+    B, T, H, D = q.shape
+    for n, t in (("q", q), ("k", k), ("q_rope", q_rope), ("k_rope", k_rope), ("v", v), ("o", o),
+                 ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _dev_tensor(t, n, torch.bfloat16, (B, T, H, D))
+    _dev_tensor(lse, "lse", torch.float32, (B, H, T))
+    if pos_offset is not None:
+        _dev_tensor(pos_offset, "pos_offset", torch.int32, (B,))
+    _dev_tensor(workspace, "workspace")
+    if workspace.numel() * workspace.element_size() < swattn_bwd_workspace_size(B, H, T, D):
+        raise SwattnError("workspace too small")
+    _check(lib().swattn_bwd_rope(_ptr(q), _ptr(k), _ptr(q_rope), _ptr(k_rope), _ptr(v), _ptr(o),
+                                 _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(pos_offset), B, H, T, D, int(window), float(scale),
+                                 float(base), float(eps), _ptr(workspace),
+                                 _stream(stream, q.device)), "swattn_bwd_rope")
 
 
 # ----------------------------------------------------------------------------- allocating wrappers

@@ -255,11 +255,13 @@ int swattn_decode_gqa(const void *q, const void *k_cache, const void *v_cache,
  *   pair i = (x_n[i], x_n[i + D/2]), i < D/2, rotated by the angle p * base^(-2i/D):
  *   y[i] = a cos - b sin, y[i + D/2] = a sin + b cos   (a, b the pair).
  * Writes y into q_out [B,T,H,D] and k_out [B,T,Hkv,D] (bf16, rounded to nearest
- * even from fp32; angles in fp64).  Hkv is independent of H here (any >= 1).
- * Outputs may be their own inputs (in place); other overlaps are not allowed.
- * INVALID_ARG: a NULL or misaligned tensor, B, T, H, Hkv <= 0, base <= 0, eps < 0
- * or either not finite, B * T > INT_MAX / 2.  UNSUPPORTED: D not 64 or 128.
- * Asynchronous on `stream`; no workspace.
+ * even from fp32; angles in fp64).  Hkv is independent of H here.  One side may be
+ * absent: H = 0 transforms k alone (q, q_out may be NULL), Hkv = 0 q alone (k, k_out
+ * may be NULL); not both.  Outputs may be their own inputs (in place); other
+ * overlaps are not allowed.
+ * INVALID_ARG: a NULL or misaligned tensor of a present side, B, T <= 0, H or Hkv < 0,
+ * H + Hkv == 0, base <= 0, eps < 0 or either not finite, B * T > INT_MAX / 2.
+ * UNSUPPORTED: D not 64 or 128.  Asynchronous on `stream`; no workspace.
  */
 int swattn_qk_norm_rope(const void *q, const void *k, void *q_out, void *k_out,
                         const int *pos_offset, int B, int T, int H, int Hkv, int D, float base,
@@ -276,6 +278,43 @@ int swattn_qk_norm_rope_bwd(const void *q, const void *k, const void *dq_out,
                             const void *dk_out, void *dq, void *dk, const int *pos_offset, int B,
                             int T, int H, int Hkv, int D, float base, float eps,
                             swattn_stream_t stream);
+
+/*
+ * Attention with the QK-norm + rotary prologue fused into the passes that hold q or k
+ * in registers (bf16, no K/V head groups: k, v [B,T,H,D]).  Same definitions as
+ * swattn_qk_norm_rope (positions, base, eps, pos_offset) and swattn_fwd / swattn_bwd;
+ * a training step through the prologue and attention becomes
+ *   swattn_qk_norm_rope(NULL, k, NULL, k_rope, pos_offset, B, T, 0, H, ...)  (keys only)
+ *   swattn_fwd_rope(q, k_rope, v, o, lse, q_rope, ...)
+ *   swattn_bwd_rope(q, k, q_rope, k_rope, v, o, dO, lse, dq, dk, dv, ...)
+ * where q and k are the raw projections and dq, dk the gradients with respect to them,
+ * instead of the two-sided prologue, swattn_fwd, swattn_bwd and swattn_qk_norm_rope_bwd.
+ * Each query (in the forward and the dQ pass) and each key (in the dK/dV pass) is
+ * normalised and rotated as it is loaded into registers; the dQ and dK/dV passes map
+ * their gradients back through the prologue in their epilogues (from fp32, with the
+ * raw rows read again), so q' and k' gradients are never stored.  The streamed sides
+ * (k_rope in the forward and the dQ pass, q_rope in the dK/dV pass) are the
+ * transformed tensors.  Sines and cosines are taken on fp64-reduced angles by the
+ * hardware's sine and cosine: q' and k' may differ from swattn_qk_norm_rope's in the
+ * last bit of the bf16 rounding.
+ *
+ * swattn_fwd_rope: q raw [B,T,H,D]; k_rope = the prologue applied to k; o, lse as
+ *   swattn_fwd.  q_rope (nullable) receives the transformed queries (bf16), which
+ *   swattn_bwd_rope streams.
+ * swattn_bwd_rope: q, k raw; q_rope, k_rope transformed; o, lse from swattn_fwd_rope;
+ *   dq, dk with respect to the raw q and k, dv as swattn_bwd.  Workspace as
+ *   swattn_bwd_workspace_size().
+ * Errors: those of swattn_fwd / swattn_bwd, and INVALID_ARG for base <= 0, eps < 0 or
+ * either not finite.
+ */
+int swattn_fwd_rope(const void *q, const void *k_rope, const void *v, void *o, float *lse,
+                    void *q_rope, const int *pos_offset, int B, int H, int T, int D, int window,
+                    float scale, float base, float eps, swattn_stream_t stream);
+int swattn_bwd_rope(const void *q, const void *k, const void *q_rope, const void *k_rope,
+                    const void *v, const void *o, const void *dO, const float *lse, void *dq,
+                    void *dk, void *dv, const int *pos_offset, int B, int H, int T, int D,
+                    int window, float scale, float base, float eps, void *workspace,
+                    swattn_stream_t stream);
 
 #ifdef __cplusplus
 }

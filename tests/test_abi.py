@@ -127,7 +127,11 @@ def test_prologue_argument_errors():
     lib = swattn.lib()
     p4, p6 = [FAKE] * 4, [FAKE] * 6
     # q, k, q_out, k_out, pos_offset, B, T, H, Hkv, D, base, eps, stream
-    assert lib.swattn_qk_norm_rope(*p4, None, 1, 8, 6, 0, 64, 1e4, 1e-6, None) == 1
+    assert lib.swattn_qk_norm_rope(*p4, None, 1, 8, 0, 0, 64, 1e4, 1e-6, None) == 1  # no side
+    assert lib.swattn_qk_norm_rope(*p4, None, 1, 8, -1, 2, 64, 1e4, 1e-6, None) == 1
+    # keys only (H = 0): q may be NULL, k may not
+    assert lib.swattn_qk_norm_rope(None, None, None, None, None, 1, 8, 0, 2, 64, 1e4, 1e-6,
+                                   None) == 1
     assert lib.swattn_qk_norm_rope(*p4, None, 0, 8, 6, 2, 64, 1e4, 1e-6, None) == 1
     assert lib.swattn_qk_norm_rope(*p4, None, 1, 8, 6, 2, 96, 1e4, 1e-6, None) == 2
     assert lib.swattn_qk_norm_rope(*p4, None, 1, 8, 6, 2, 64, 0.0, 1e-6, None) == 1
@@ -186,3 +190,22 @@ def test_noalloc_decode_checks_before_touching_the_gpu():
     assert lib.swattn_decode_noalloc(*p6, 32, 12, 128, 20000, -1, 1.0, None) == 4
     # the decode workload (4096-row caches) fits: 6.3 MB
     assert swattn.swattn_decode_workspace_size(32, 12, 128, 4096, -1) <= 16 << 20
+
+
+def test_fused_rope_argument_errors():
+    """swattn_fwd_rope / swattn_bwd_rope check sizes, scale, base and eps before any launch."""
+    lib = swattn.lib()
+    p5 = [FAKE] * 5
+    # q, k_rope, v, o, lse, q_rope, pos_offset, B, H, T, D, window, scale, base, eps, stream
+    assert lib.swattn_fwd_rope(*p5, None, None, 1, 2, 8, 64, 0, 0.1, 1e4, 1e-6, None) == 1
+    assert lib.swattn_fwd_rope(*p5, None, None, 1, 2, 8, 96, -1, 0.1, 1e4, 1e-6, None) == 2
+    assert lib.swattn_fwd_rope(*p5, None, None, 1, 2, 8, 64, -1, 0.1, 0.0, 1e-6, None) == 1
+    assert lib.swattn_fwd_rope(*p5, None, None, 1, 2, 8, 64, -1, 0.1, 1e4, -1.0, None) == 1
+    assert lib.swattn_fwd_rope(*p5, MISALIGNED, None, 1, 2, 8, 64, -1, 0.1, 1e4, 0.0, None) == 1
+    p11 = [FAKE] * 11
+    # q, k, q_rope, k_rope, v, o, dO, lse, dq, dk, dv, pos_offset, B, H, T, D, window, scale,
+    # base, eps, workspace, stream
+    assert lib.swattn_bwd_rope(*p11, None, 1, 2, 8, 64, -1, 0.0, 1e4, 1e-6, FAKE, None) == 1
+    assert lib.swattn_bwd_rope(*p11, None, 1, 2, 8, 64, -1, 0.1, float("nan"), 1e-6, FAKE,
+                               None) == 1
+    assert lib.swattn_bwd_rope(*p11, None, 1, 2, 8, 64, -1, 0.1, 1e4, 1e-6, None, None) == 1
