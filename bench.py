@@ -676,11 +676,7 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
 
     copy_f = copy_reading(fetch_csv, "FETCH_SIZE")
     copy_w = copy_reading(write_csv, "WRITE_SIZE")
-    # the training and decode kernels of the small and decode workloads (not the grouped
-    # or prefill instantiations, which the same run also launches)
-    names = {"fwd": "fwd_bf16_kernel<128, false>",
-             "bwd_dkdv": "bwd_dkdv_bf16_kernel<128, false>", "bwd_dq": "bwd_dq_bf16_kernel<128>",
-             "decode_split": "decode_split_kernel<unsigned short, 128, false>"}
+    names = {n: SQ_NAMES[n] for n in ("fwd", "bwd_dkdv", "bwd_dq", "decode_split")}
     out = {"source_hash": source_hash(), "copy_bytes": copy_bytes,
            "fetch_factor": copy_bytes / copy_f if copy_f else 1.0,
            "write_factor": copy_bytes / copy_w if copy_w else 1.0, "kernels": {}}
@@ -699,8 +695,10 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
     print(json.dumps(out))
 
 
-SQ_NAMES = {"fwd": "fwd_bf16_kernel<128, false>", "bwd_dq": "bwd_dq_bf16_kernel<128>",
-            "bwd_dkdv": "bwd_dkdv_bf16_kernel<128, false>",
+# the training kernels of the small workload (not the grouped, prefill, fused-prologue or
+# short-window instantiations, which the same runs may launch), matched by name prefix
+SQ_NAMES = {"fwd": "fwd_bf16_kernel<128, false, false", "bwd_dq": "bwd_dq_bf16_kernel<128, false>",
+            "bwd_dkdv": "bwd_dkdv_bf16_kernel<128, false, false>",
             "decode_split": "decode_split_kernel<unsigned short, 128, false>",
             "decode_merge": "decode_merge_kernel<unsigned short, 128>"}
 
