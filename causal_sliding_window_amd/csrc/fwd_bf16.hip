@@ -4,7 +4,8 @@
 // LSE per query row: the attention call of the nanochat guide's section 5 ("Flash
 // Attention unification") with the sliding window of its section 1 feature list.
 //
-// Work decomposition (one workgroup = 4 waves = 128 queries of one (b, h)):
+// Work decomposition (one workgroup = NW waves = 32 NW queries of one (b, h); NW = 4,
+// or 2 for short windows):
 //   * each wave owns 32 queries; its Q block stays in registers as the MFMA B
 //     operand of S^T = K Q^T (32 keys x 32 queries per MFMA tile), so a lane owns
 //     one query and the row statistics are per lane plus one cross-half exchange;
@@ -39,16 +40,22 @@
 
 namespace swattn {
 
-template <int D>
+template <int D, int NW = 4>
 struct FwdCfg {
-  static constexpr int BM = 128;               // queries per workgroup (4 waves x 32)
+  static constexpr int BM = 32 * NW;           // queries per workgroup (NW waves x 32)
   static constexpr int BN = 32;                // keys per tile
   static constexpr int KST = D / 16;           // k-steps of S over D
   static constexpr int NDB = D / 32;           // 32-column blocks of D
   static constexpr int TSZ = BN * D;           // elements of one K or V tile
   static constexpr int RG = BN / 16;           // 16-row groups per 32-column block
-  static constexpr int CPW = TSZ * 2 / 1024 / 4;  // 1-KB copies per wave and tile
+  static constexpr int CPW = TSZ * 2 / 1024 / NW;  // 1-KB copies per wave and tile
 };
+
+// Short windows: a workgroup steps through every key tile of its waves' bands, and each
+// wave computes only those of its own band.  With windows up to this size the forward
+// takes workgroups of 2 waves (64 queries), whose bands overlap more: at W = 256 a wave
+// computes 9 of the 10 tiles its workgroup visits, against 9 of 12 with 4 waves.
+constexpr int kShortWindow = 512;
 
 // Prefill: up to this many sequences, workgroups take (sequence, query tile) items
 // longest first, ranked on the device by cache offset.
@@ -59,13 +66,13 @@ constexpr float kRescaleLog2 = 8.f;
 
 // ROPE: q holds the raw queries; each is normalised and rotated (QK norm + rotary
 // embedding) as it is loaded into registers, and written to q_rope when that is not null.
-template <int D, bool PREFILL, bool ROPE = false>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+template <int D, bool PREFILL, bool ROPE = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
     const int *__restrict__ seqlens, int B, int H, int Hkv, int T, int Tkv, int window,
     float scale, int nqt, RopeArgs ra = RopeArgs{}, uint16_t *__restrict__ q_rope = nullptr) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, NW>;
   // [slot][K, V][TSZ]
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * C::TSZ];
 
@@ -431,19 +438,30 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   }
 }
 
+template <int D, int NW>
+static void launch_fwd_t(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                         int H, int Hkv, int T, int window, float scale, hipStream_t st) {
+  const int nqt = (T + FwdCfg<D, NW>::BM - 1) / FwdCfg<D, NW>::BM;
+  fwd_bf16_kernel<D, false, false, NW><<<dim3((unsigned)(nqt * B * H)), dim3(64 * NW), 0, st>>>(
+      (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr,
+      B, H, Hkv, T, T, window, scale, nqt);
+}
+
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                            int B, int H, int Hkv, int T, int D, int window, float scale,
                            hipStream_t st) {
-  const int nqt = (T + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
-  dim3 grid((unsigned)(nqt * B * H)), block(256);
-  if (D == 128)
-    fwd_bf16_kernel<128, false><<<grid, block, 0, st>>>(
-        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr,
-        B, H, Hkv, T, T, window, scale, nqt);
-  else
-    fwd_bf16_kernel<64, false><<<grid, block, 0, st>>>(
-        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr,
-        B, H, Hkv, T, T, window, scale, nqt);
+  const bool short_w = window > 0 && window <= kShortWindow && window < T;
+  if (D == 128) {
+    if (short_w)
+      launch_fwd_t<128, 2>(q, k, v, o, lse, B, H, Hkv, T, window, scale, st);
+    else
+      launch_fwd_t<128, 4>(q, k, v, o, lse, B, H, Hkv, T, window, scale, st);
+  } else {
+    if (short_w)
+      launch_fwd_t<64, 2>(q, k, v, o, lse, B, H, Hkv, T, window, scale, st);
+    else
+      launch_fwd_t<64, 4>(q, k, v, o, lse, B, H, Hkv, T, window, scale, st);
+  }
   return hipGetLastError();
 }
 
