@@ -3,7 +3,7 @@
 // read).  Bound by HBM: every visible K/V cache row is read exactly once.
 //
 // decode_split_kernel: workgroup (K/V head hk, chunk c, sequence b) reads seqlens[b]
-//   on the device, takes its kDecodeChunk rows of the visible range
+//   on the device, takes its kDecodeChunkWide rows (8 waves of 32) of the visible range
 //   [max(0, L - W), L), and for each query head that reads K/V head hk (H / Hkv of
 //   them; one without grouping) writes a partial (o_c normalised, lse_c) to the
 //   workspace (or o and lse directly when the visible range is one chunk).  The
@@ -99,8 +99,8 @@ __device__ __forceinline__ float across_groups_sum(float x) {
 // GROUPED: more than one query head per K/V head (H > Hkv).  Without it the head loop
 // has one trip known at compile time, and the K/V rows need not stay in registers
 // after their use.
-template <typename TT, int D, bool GROUPED>
-__global__ __launch_bounds__(256) void decode_split_kernel(
+template <typename TT, int D, bool GROUPED, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void decode_split_kernel(
     const TT *__restrict__ q, const TT *__restrict__ kc, const TT *__restrict__ vc,
     const int *__restrict__ seqlens, float *__restrict__ ws_o, float *__restrict__ ws_lse,
     TT *__restrict__ o, float *__restrict__ lse, int H, int Hkv, int Tmax, int window,
@@ -108,12 +108,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   constexpr int EPL = Elem<TT>::PER16;  // elements per 16-byte load
   constexpr int LPR = D / EPL;          // lanes per cache row
   constexpr int GPW = 64 / LPR;         // rows per wave and round
-  constexpr int CH = kDecodeChunk;      // rows per workgroup
-  constexpr int TPW = CH / 4;           // rows per wave
+  constexpr int CH = 32 * NW;          // rows per workgroup
+  constexpr int TPW = 32;               // rows per wave
   constexpr int ROUNDS = TPW / GPW;
-  constexpr int GB = GROUPED ? kDecodeHeadBatch : 1;  // query heads merged per batch
-  __shared__ float part_o[4][GB][D];
-  __shared__ float part_ml[4][GB][2];
+  // query heads merged per batch (the LDS partials hold NW x GB rows of D floats)
+  constexpr int GB = GROUPED ? kDecodeHeadBatch * 4 / NW : 1;
+  __shared__ float part_o[NW][GB][D];
+  __shared__ float part_ml[NW][GB][2];
 
   // K/V heads vary fastest across workgroups: the workgroups reading the rows of one
   // token range (adjacent 256-byte pieces of the same cache lines' DRAM pages) run together
@@ -217,22 +218,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       }
     }
     __syncthreads();
-    // merge the four wave partials of each head (a wave without visible rows has
+    // merge the NW wave partials of each head (a wave without visible rows has
     // m = -inf, l = 0); m is in exp2 units, lse in natural log
-    for (int i = tid; i < gn * D; i += 256) {
+    for (int i = tid; i < gn * D; i += 64 * NW) {
       const int j = i / D, d = i % D;
       const int bh = b * H + hk * G + g0 + j;
       float M = part_ml[0][j][0];
 #pragma unroll
-      for (int u = 1; u < 4; ++u) M = fmaxf(M, part_ml[u][j][0]);
-      float f[4], Ltot = 0.f, ov = 0.f;
+      for (int u = 1; u < NW; ++u) M = fmaxf(M, part_ml[u][j][0]);
+      float f[NW], Ltot = 0.f, ov = 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < NW; ++u) {
         f[u] = part_ml[u][j][0] == -INFINITY ? 0.f : fast_exp2(part_ml[u][j][0] - M);
         Ltot += f[u] * part_ml[u][j][1];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) ov += f[u] * part_o[u][j][d];
+      for (int u = 0; u < NW; ++u) ov += f[u] * part_o[u][j][d];
       ov /= Ltot;
       const size_t slot = (size_t)bh * nsplit + c;
       if (nch == 1) o[(size_t)bh * D + d] = Elem<TT>::pack(ov);  // nothing to merge
@@ -257,7 +258,7 @@ template <typename TT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float *__restrict__ ws_o, const float *__restrict__ ws_lse,
     const int *__restrict__ seqlens, TT *__restrict__ o, float *__restrict__ lse, int H, int Tmax,
-    int window, int nsplit) {
+    int window, int nsplit, int chunk) {
   constexpr int G = 256 / D;
   constexpr int MB = 16;  // chunks per thread and batch
   __shared__ float red[4];
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int L = min(seqlens[b], Tmax);
   if (L <= 0) return;
   const int n = L - visible_lo(L, window);
-  const int nch = (n + kDecodeChunk - 1) / kDecodeChunk;
+  const int nch = (n + chunk - 1) / chunk;
   if (nch <= 1) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = tid / D, d = tid % D;
@@ -539,24 +540,38 @@ static hipError_t launch_decode_t(const void *q, const void *k_cache, const void
                                   const int *seqlens, void *o, float *lse, int B, int H,
                                   int Hkv, int Tmax, int window, float scale, float *ws,
                                   hipStream_t st) {
-  const int ns = decode_num_splits(Tmax, window);
+  // the workspace holds decode_num_splits(Tmax, window) partials per (b, h): enough for
+  // the kDecodeChunk-row chunks of the matrix-core kernel; the vector split kernel takes
+  // chunks of kDecodeChunkWide rows, half as many
+  const int ns_ws = decode_num_splits(Tmax, window);
   float *ws_o = ws;
-  float *ws_lse = ws + (size_t)B * H * ns * D;
-  if (std::is_same<TT, uint16_t>::value && D == 128 && H >= kGqaMfmaMinGroup * Hkv)
+  float *ws_lse = ws + (size_t)B * H * ns_ws * D;
+  int ns = ns_ws, chunk = kDecodeChunk;
+  if (std::is_same<TT, uint16_t>::value && D == 128 && H >= kGqaMfmaMinGroup * Hkv) {
     decode_gqa_mfma_kernel<<<dim3(Hkv, ns, B), 256, 0, st>>>(
         (const uint16_t *)q, (const uint16_t *)k_cache, (const uint16_t *)v_cache, seqlens, ws_o,
         ws_lse, (uint16_t *)o, lse, H, Hkv, Tmax, window, scale, ns);
-  else if (Hkv != H)
-    decode_split_kernel<TT, D, true><<<dim3(Hkv, ns, B), 256, 0, st>>>(
-        (const TT *)q, (const TT *)k_cache, (const TT *)v_cache, seqlens, ws_o, ws_lse, (TT *)o,
-        lse, H, Hkv, Tmax, window, scale, ns);
-  else
-    decode_split_kernel<TT, D, false><<<dim3(Hkv, ns, B), 256, 0, st>>>(
-        (const TT *)q, (const TT *)k_cache, (const TT *)v_cache, seqlens, ws_o, ws_lse, (TT *)o,
-        lse, H, Hkv, Tmax, window, scale, ns);
+  } else {
+    // the vector kernels, grouped or not, take the same kDecodeChunkWide-row chunks:
+    // one query head's arithmetic is then the same on both (at D = 64 the grouped
+    // decode of a cache equals the ungrouped decode of that cache repeated over the group)
+    constexpr int NWW = kDecodeChunkWide / 32;
+    chunk = kDecodeChunkWide;
+    const int vis = window > 0 ? (window < Tmax ? window : Tmax) : Tmax;
+    ns = (vis + chunk - 1) / chunk;
+    if (Hkv != H)
+      decode_split_kernel<TT, D, true, NWW><<<dim3(Hkv, ns, B), 64 * NWW, 0, st>>>(
+          (const TT *)q, (const TT *)k_cache, (const TT *)v_cache, seqlens, ws_o, ws_lse,
+          (TT *)o, lse, H, Hkv, Tmax, window, scale, ns);
+    else
+      decode_split_kernel<TT, D, false, NWW><<<dim3(Hkv, ns, B), 64 * NWW, 0, st>>>(
+          (const TT *)q, (const TT *)k_cache, (const TT *)v_cache, seqlens, ws_o, ws_lse,
+          (TT *)o, lse, H, Hkv, Tmax, window, scale, ns);
+  }
+  // partials of (b, h) at slots b h ns .. + ns - 1 (ns <= ns_ws)
   if (ns > 1)
     decode_merge_kernel<TT, D><<<B * H, 256, 0, st>>>(ws_o, ws_lse, seqlens, (TT *)o, lse, H, Tmax,
-                                                      window, ns);
+                                                      window, ns, chunk);
   return hipGetLastError();
 }
 

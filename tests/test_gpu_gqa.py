@@ -185,6 +185,29 @@ def test_gqa_decode_chunk_edges(H, Hkv, W):
     check("lse", lse, rl, torch.bfloat16, lse=True)
 
 
+_EDGES = [0, 1, 2, 127, 128, 129, 255, 256, 257, 383, 384, 385, 511, 512, 513, 767, 768, 769,
+          1023, 1024, 1025, 2047, 2048, 3000, 4095, 4096]
+
+
+@pytest.mark.parametrize("B,H,Hkv,Tmax,W", [(32, 24, 8, 1024, -1), (32, 12, 4, 4096, -1),
+                                            (32, 64, 2, 4096, -1), (128, 24, 8, 512, 129),
+                                            (128, 24, 8, 512, 300), (64, 12, 4, 2048, 1000)])
+def test_gqa_decode_large_grids(B, H, Hkv, Tmax, W):
+    """Grids of 1024 and more workgroups on the matrix-core kernel (B Hkv ceil(visible /
+    256) >= 1024): groups of 3, 12 and 32 heads, up to 128 sequences; lengths on and next
+    to the 128- and 256-row edges, an empty sequence, lengths past the window."""
+    lens = [0] + [min(_EDGES[1 + i % (len(_EDGES) - 1)], Tmax) for i in range(B - 1)]
+    d = inputs.decode_inputs(B, H, 128, Tmax, "bf16", seed=B + H + W, lengths=lens, Hkv=Hkv)
+    g = _gpu(d)
+    scale = 1 / math.sqrt(128)
+    o, lse = swattn.decode(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], W, scale)
+    torch.cuda.synchronize()
+    ro, rl = _decode_oracle(d, W, scale)
+    check("o", o, ro, torch.bfloat16)
+    assert torch.all(o[0] == 0) and torch.all(lse[0] == -math.inf)  # the empty sequence
+    check("lse", lse[1:], rl[1:], torch.bfloat16, lse=True)
+
+
 def test_gqa_decode_long_cache_mqa():
     """One K/V head for all query heads (multi-query), 20000-row caches."""
     lens = [20000, 9001]

@@ -228,9 +228,11 @@ def test_decode_config(W):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("W", [-1, 1, 100, 300])
+@pytest.mark.parametrize("W", [-1, 1, 100, 256, 257, 300])
 def test_decode_shapes(dtype, D, W):
-    lens = [1, 2, 255, 256, 257, 511, 700, 700]
+    """Lengths and windows on and next to the edges of the split kernel's 256-row
+    chunks (one, two and three chunks per sequence)."""
+    lens = [1, 2, 255, 256, 257, 511, 512, 513, 700, 700]
     d = inputs.decode_inputs(len(lens), 3, D, 700, dtype, seed=D + W, lengths=lens)
     g = _gpu(d)
     scale = 1 / math.sqrt(D)
@@ -242,10 +244,31 @@ def test_decode_shapes(dtype, D, W):
     check("lse", lse, rl, td, lse=True)
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+@pytest.mark.parametrize("W,Tmax", [(-1, 1024), (1024, 1500), (300, 1100), (1, 600)])
+def test_decode_many_heads_short_ranges(dtype, D, W, Tmax):
+    """24 x 12 = 288 (b, h) pairs, more than one per compute unit, with visible ranges of
+    at most 1024 rows (one to four 256-row chunks): lengths on and next to the chunk
+    edges, an empty sequence, and lengths past the window."""
+    base = [0, 1, 2, 255, 256, 257, 511, 512, 513, 767, 768, 769, 1023, 1024, 1025, 1100,
+            1300, 1499, 1500, 40, 600, 700, 900, 1000]
+    lens = [min(x, Tmax) for x in base]
+    d = inputs.decode_inputs(len(lens), 12, D, Tmax, dtype, seed=D + W + Tmax, lengths=lens)
+    g = _gpu(d)
+    scale = 1 / math.sqrt(D)
+    o, lse = swattn.decode(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], W, scale)
+    torch.cuda.synchronize()
+    ro, rl = _decode_oracle(d, W, scale)
+    td = inputs.DTYPES[dtype]
+    assert torch.all(o[0] == 0) and torch.all(lse[0] == -math.inf)  # the empty sequence
+    check("o", o, ro, td)
+    check("lse", lse[1:], rl[1:], td, lse=True)
+
+
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
 @pytest.mark.parametrize("W", [-1, 9000])
 def test_decode_long_cache(dtype, D, W):
-    """Caches of 20000 rows: up to 157 chunks of 128 rows per sequence, so the merge
+    """Caches of 20000 rows: up to 79 chunks of 256 rows per sequence, so the merge
     runs several batches of chunks per thread (D = 128: 32 chunks per batch; D = 64:
     64)."""
     lens = [20000, 9001, 4097]
