@@ -335,10 +335,28 @@ def bench_decode(torch, swattn, inputs, iters, hkv=None):
         nbytes = decode_bytes(lengths, H, D, W, Hkv=hkv)
         ms = statistics.median(cold)
         gbs = nbytes / (ms * 1e-3) / 1e9
+        # a cold device copy moving the same bytes (half read, half written), timed alike
+        src = torch.ones(nbytes // 2, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        cp = []
+        for _ in range(iters):
+            flush.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dst.copy_(src)
+            b.record()
+            torch.cuda.synchronize()
+            cp.append(a.elapsed_time(b))
+        del src, dst
+        ms_copy = statistics.median(cp)
         out["causal" if W < 0 else f"window{W}"] = {
             "bytes": nbytes, "us_cold_median": round(ms * 1e3, 2),
             "us_warm_median": round(statistics.median(warm) * 1e3, 2),
             "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "cold_copy_same_bytes_us": round(ms_copy * 1e3, 2),
+            "frac_of_cold_copy": round(ms_copy / ms, 4),
         }
     return out
 
@@ -347,7 +365,9 @@ def bench_prologue(torch, swattn, inputs, iters, cfg_name="small"):
     """QK-norm + rotary prologue on a training workload's raw q and k (one launch for
     both), forward and backward, cold (a 1 GiB fill before each call).  Bytes: the
     forward reads q, k and writes q', k'; the backward reads q, k, dq', dk' and writes
-    dq, dk."""
+    dq, dk.  Next to each, a cold device copy (torch) that moves the same number of
+    bytes (half read, half written), timed the same way: the practical ceiling of one
+    cold pass of that size on this GPU."""
     c = inputs.CONFIGS[cfg_name]
     B, T, H, D = c["B"], c["T"], c["H"], c["D"]
     x = inputs.training_inputs(B, T, H, D, c["dtype"], c["seeds"][0], qk_norm=False)
@@ -360,7 +380,7 @@ def bench_prologue(torch, swattn, inputs, iters, cfg_name="small"):
              "backward": lambda: swattn.swattn_qk_norm_rope_bwd(q, k, dyq, dyk, dq, dk)}
     tensor_bytes = q.numel() * q.element_size()
     res = {"workload": f"{cfg_name}: q and k [{B},{T},{H},{D}] bf16, raw"}
-    for name, call in calls.items():
+    def cold_ms(call):
         for _ in range(3):
             call()
         ts = []
@@ -372,11 +392,20 @@ def bench_prologue(torch, swattn, inputs, iters, cfg_name="small"):
             b.record()
             torch.cuda.synchronize()
             ts.append(a.elapsed_time(b))
+        return statistics.median(ts)
+
+    for name, call in calls.items():
         nb = (4 if name == "forward" else 6) * tensor_bytes
-        ms = statistics.median(ts)
+        ms = cold_ms(call)
+        src = torch.ones(nb // 2, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        ms_copy = cold_ms(lambda: dst.copy_(src))
+        del src, dst
         res[name] = {"bytes": nb, "us_cold_median": round(ms * 1e3, 2),
                      "GB_per_s": round(nb / (ms * 1e-3) / 1e9, 1),
-                     "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                     "frac_hbm_peak": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "cold_copy_same_bytes_us": round(ms_copy * 1e3, 2),
+                     "frac_of_cold_copy": round(ms_copy / ms, 4)}
     del flush
     return res
 
@@ -545,9 +574,12 @@ def bench_training_gqa(torch, swattn, inputs, cfg_name, hkv, steps, warmup):
             "bwd_TFLOP_per_s": round(acct["flops_bwd"] / (per["bwd"] * 1e-3) / 1e12, 1)}
 
 
-def measured_refs(torch):
+def measured_refs(torch, swattn):
     """Practical ceilings measured on this GPU, reported next to the published peaks: a
-    1 GiB device copy (read + write bytes) and an 8192^3 bf16 GEMM (torch.matmul)."""
+    1 GiB device copy (read + write bytes) and an 8192^3 bf16 GEMM (torch.matmul), and
+    the library's own probes: the rate of back-to-back 32x32x16 bf16 matrix products
+    (two waves per SIMD, operands in registers, no memory traffic) and the rate of one
+    streaming pass of non-temporal 16-byte reads over 1 GiB."""
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def timed(fn, n=10):
@@ -575,9 +607,37 @@ def measured_refs(torch):
     y = torch.randn(m, m, device="cuda:0", generator=g).to(torch.bfloat16)
     t_mm = timed(lambda: torch.matmul(x, y))
     del x, y
+    # the probes at two or three grid sizes each; the best rate is the ceiling
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 20000
+    mfma = {}
+    for per_cu in (2, 4):  # two and four waves per SIMD
+        wg = per_cu * cus
+        pout = torch.empty(wg * 256, dtype=torch.float32, device="cuda:0")
+        t_mfma = timed(lambda: swattn.swattn_probe_mfma(pout, wg, iters))
+        torch.cuda.synchronize()
+        assert bool(torch.all(pout == iters / 64)), "MFMA probe: wrong products"
+        mfma[per_cu] = wg * 4 * iters * 4 * 32768 / t_mfma / 1e12
+        del pout
+    nb = 1 << 30
+    buf = torch.ones(nb // 4, dtype=torch.int32, device="cuda:0")
+    read = {}
+    for per_cu in (2, 4, 8):
+        rwg = per_cu * cus
+        rout = torch.empty(rwg * 256, dtype=torch.int32, device="cuda:0")
+        read[per_cu] = nb / timed(lambda: swattn.swattn_probe_read(buf, rout, rwg)) / 1e9
+        del rout
+    del buf
     return {"copy_GB_per_s": round(2 * n * 4 / t_copy / 1e9, 1),
             "gemm_bf16_TFLOP_per_s": round(2 * m ** 3 / t_mm / 1e12, 1),
-            "what": "1 GiB device copy (read + write bytes); 8192^3 bf16 torch.matmul"}
+            "mfma_probe_TFLOP_per_s": round(max(mfma.values()), 1),
+            "read_probe_GB_per_s": round(max(read.values()), 1),
+            "probe_rates": {"mfma_TFLOP_per_s_by_workgroups_per_CU": {k: round(v, 1) for k, v in mfma.items()},
+                            "read_GB_per_s_by_workgroups_per_CU": {k: round(v, 1) for k, v in read.items()}},
+            "what": "1 GiB device copy (read + write bytes); 8192^3 bf16 torch.matmul; "
+                    "swattn_probe_mfma (32x32x16 bf16 back to back, 4 waves per workgroup); "
+                    "swattn_probe_read (one non-temporal pass over 1 GiB, contiguous span "
+                    "per workgroup); the best rate of each probe"}
 
 
 # ----------------------------------------------------------------------------- CPU oracle leg
@@ -699,7 +759,7 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
 # short-window instantiations, which the same runs may launch), matched by name prefix
 SQ_NAMES = {"fwd": "fwd_bf16_kernel<128, false, false", "bwd_dq": "bwd_dq_bf16_kernel<128, false>",
             "bwd_dkdv": "bwd_dkdv_bf16_kernel<128, false, false>",
-            "decode_split": "decode_split_kernel<unsigned short, 128, false>",
+            "decode_split": "decode_split_kernel<unsigned short, 128, false, ",
             "decode_merge": "decode_merge_kernel<unsigned short, 128>"}
 
 
@@ -878,11 +938,13 @@ def main():
                                                  max(50, args.steps // 4), max(50, args.warmup // 2))
         log(f"training gqa {res['training_gqa']}")
     if not args.no_refs:
-        refs = measured_refs(torch)
+        refs = measured_refs(torch, swattn)
         res["measured_refs"] = refs
         res["roofline"]["frac_of_measured_gemm"] = round(achieved / refs["gemm_bf16_TFLOP_per_s"], 4)
+        res["roofline"]["frac_of_mfma_probe"] = round(achieved / refs["mfma_probe_TFLOP_per_s"], 4)
         for d in res.get("decode", {}).values():
             d["frac_of_measured_copy"] = round(d["GB_per_s"] / refs["copy_GB_per_s"], 4)
+            d["frac_of_read_probe"] = round(d["GB_per_s"] / refs["read_probe_GB_per_s"], 4)
         log(f"measured refs {refs}")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inputs)

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libswattn.so")
 SOURCES = ["api.hip", "fwd_bf16.hip", "bwd_bf16.hip", "dkdv_bf16.hip", "decode.hip", "f32.hip",
-           "prologue.hip", "noalloc.hip"]
+           "prologue.hip", "noalloc.hip", "probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

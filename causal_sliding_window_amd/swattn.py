@@ -55,6 +55,8 @@ _SIGS = {
     "swattn_qk_norm_rope_bwd": ([_P] * 7 + [_I] * 5 + [_F, _F, _P], _I),
     "swattn_fwd_rope": ([_P] * 7 + [_I] * 5 + [_F, _F, _F, _P], _I),
     "swattn_bwd_rope": ([_P] * 12 + [_I] * 5 + [_F, _F, _F, _P, _P], _I),
+    "swattn_probe_mfma": ([_P, _I, _I, _P], _I),
+    "swattn_probe_read": ([_P, ctypes.c_size_t, _P, _I, _P], _I),
 }
 
 
@@ -248,6 +250,26 @@ def swattn_decode_noalloc(q, k_cache, v_cache, seqlens, o, lse, window: int, sca
                                        _ptr(o), _ptr(lse), B, H, D, Tmax, int(window),
                                        float(scale), _stream(stream, q.device)),
            "swattn_decode_noalloc")
+
+
+# ----------------------------------------------------------------------------- measurement probes
+def swattn_probe_mfma(out, workgroups: int, iters: int, stream=None):
+    """Matrix-core rate probe: out float32 [workgroups * 256] (device); flops =
+    workgroups * 4 * iters * 4 * 32768; every element of out becomes iters / 64."""
+    _dev_tensor(out, "out", torch.float32, (workgroups * 256,))
+    _check(lib().swattn_probe_mfma(_ptr(out), int(workgroups), int(iters),
+                                   _stream(stream, out.device)), "swattn_probe_mfma")
+
+
+def swattn_probe_read(src, out, workgroups: int, stream=None):
+    """Streaming-read probe over the bytes of the contiguous device tensor src; out
+    int32 [workgroups * 256] (device) receives per-thread XORs of the words read."""
+    if not (src.is_cuda and src.is_contiguous()):
+        raise SwattnError("src must be a contiguous device tensor")
+    _dev_tensor(out, "out", torch.int32, (workgroups * 256,))
+    _check(lib().swattn_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(out),
+                                   int(workgroups), _stream(stream, src.device)),
+           "swattn_probe_read")
 
 
 # ----------------------------------------------------------------------------- grouped-query entries

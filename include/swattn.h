@@ -316,6 +316,32 @@ int swattn_bwd_rope(const void *q, const void *k, const void *q_rope, const void
                     int window, float scale, float base, float eps, void *workspace,
                     swattn_stream_t stream);
 
+/*
+ * Measurement probes: what this GPU sustains, next to its published peaks (not part of
+ * the attention method; used to report the kernels against measured ceilings).
+ *
+ * swattn_probe_mfma: `workgroups` workgroups of 256 threads (4 waves each); every wave
+ *   issues iters x 4 bf16 matrix products of 32 x 32 x 16 (2 * 32 * 32 * 16 flops
+ *   each), the instruction the attention passes use, back to back on four independent
+ *   accumulator chains, with no memory traffic.  Total flops:
+ *   workgroups * 4 * iters * 4 * 32768.  out: device float32 [workgroups * 256]; every
+ *   element becomes iters / 64 (all operands 1/256: exact), which checks the products.
+ *   INVALID_ARG for a NULL or misaligned out, workgroups outside [1, 2^20], iters
+ *   outside [1, 2^24].
+ * swattn_probe_read: reads nbytes of device memory at src once, 16 bytes per lane and
+ *   load, non-temporal (as the decode kernels read the cache), eight loads in flight
+ *   per lane, in a grid of `workgroups` workgroups of 256 threads, each streaming its
+ *   own contiguous span (the buffer cut into `workgroups` equal spans, the last one
+ *   shorter); out: device uint32 [workgroups * 256], each the XOR of the 32-bit words
+ *   its thread read (the XOR of all of out is the XOR of the buffer).  INVALID_ARG for
+ *   NULL pointers, src not 16-byte aligned, nbytes 0 or not a multiple of 16,
+ *   workgroups outside [1, 2^20].
+ * Both only enqueue work on `stream`; time them with events on that stream.
+ */
+int swattn_probe_mfma(float *out, int workgroups, int iters, swattn_stream_t stream);
+int swattn_probe_read(const void *src, size_t nbytes, unsigned int *out, int workgroups,
+                      swattn_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

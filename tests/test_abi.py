@@ -209,3 +209,20 @@ def test_fused_rope_argument_errors():
     assert lib.swattn_bwd_rope(*p11, None, 1, 2, 8, 64, -1, 0.1, float("nan"), 1e-6, FAKE,
                                None) == 1
     assert lib.swattn_bwd_rope(*p11, None, 1, 2, 8, 64, -1, 0.1, 1e4, 1e-6, None, None) == 1
+
+
+def test_probe_argument_errors():
+    """The measurement probes check their arguments before anything is enqueued."""
+    lib = swattn.lib()
+    assert lib.swattn_probe_mfma(None, 1, 1, None) == 1                     # NULL out
+    assert lib.swattn_probe_mfma(MISALIGNED, 1, 1, None) == 1               # misaligned out
+    assert lib.swattn_probe_mfma(FAKE, 0, 1, None) == 1                     # no workgroups
+    assert lib.swattn_probe_mfma(FAKE, (1 << 20) + 1, 1, None) == 1         # too many
+    assert lib.swattn_probe_mfma(FAKE, 1, 0, None) == 1                     # no iterations
+    assert lib.swattn_probe_mfma(FAKE, 1, (1 << 24) + 1, None) == 1         # past exactness
+    assert lib.swattn_probe_read(None, 16, FAKE, 1, None) == 1              # NULL src
+    assert lib.swattn_probe_read(FAKE, 16, None, 1, None) == 1              # NULL out
+    assert lib.swattn_probe_read(ctypes.c_void_p((1 << 20) + 8), 16, FAKE, 1, None) == 1
+    assert lib.swattn_probe_read(FAKE, 0, FAKE, 1, None) == 1               # nothing to read
+    assert lib.swattn_probe_read(FAKE, 24, FAKE, 1, None) == 1              # not 16-byte pieces
+    assert lib.swattn_probe_read(FAKE, 16, FAKE, 0, None) == 1              # no workgroups

@@ -1,0 +1,55 @@
+"""CPU checks of the comparison helper the GPU tests use (tests/parity.py): each bar
+fails where it should, so a green GPU run means what the bars say."""
+
+import numpy as np
+import pytest
+import torch
+
+from parity import TOL_BF16_ABS, bf16_ulps, check
+
+BF = torch.bfloat16
+
+
+def test_plain_bf16_bars():
+    ref = np.linspace(-2.0, 2.0, 1001)
+    ref[7] = np.nan  # entries the oracle did not compute are skipped
+    one = np.zeros_like(ref)
+    one[3] = 1.0
+    check("ok", np.where(np.isnan(ref), 7.0, ref + 0.019 * one), ref, BF)
+    with pytest.raises(AssertionError, match="max-abs"):
+        check("abs", ref + 0.021 * one, ref, BF)
+    with pytest.raises(AssertionError, match="rel-L2"):
+        check("rel", ref * 1.006, ref, BF)
+    bad = ref.copy()
+    bad[5] = np.nan
+    with pytest.raises(AssertionError, match="non-finite"):
+        check("nan", bad, ref, BF)
+
+
+def test_lse_and_f32_bars():
+    ref = np.array([1.0, 3.0])
+    check("lse", ref + 9e-4, ref, BF, lse=True)
+    with pytest.raises(AssertionError):
+        check("lse", ref + 1.1e-3, ref, BF, lse=True)
+    check("f32", ref + 9e-6, ref, torch.float32)
+    with pytest.raises(AssertionError):
+        check("f32", ref + 1.1e-5, ref, torch.float32)
+
+
+def test_out_ulp_bar_applies_on_top_of_rounding_only_for_large_values():
+    ref = np.array([1.0, 5.0, 9.0, 3.9, np.nan])
+    # 9 + 0.035: 0.035 - 9 / 512 = 0.0174 <= 2e-2 on top of the output's rounding
+    check("large", np.array([1.01, 5.02, 9.035, 3.9, 0.0]), ref, BF, out_ulp=True)
+    # beyond the bar on top of rounding
+    with pytest.raises(AssertionError, match="2\\^-9"):
+        check("large", np.array([1.0, 5.0, 9.04, 3.9, 0.0]), ref, BF, out_ulp=True)
+    # |ref| < 4: 0.0255 - 3.9 / 512 = 0.0179 passes the relaxed form but not the plain bar
+    with pytest.raises(AssertionError, match="where \\|ref\\| < 4"):
+        check("small", np.array([1.0, 5.0, 9.0, 3.9255, 0.0]), ref, BF, out_ulp=True)
+
+
+def test_bf16_ulps():
+    # spacing of bf16 at 1.0 is 2^-7, at 9.0 it is 2^-4
+    assert bf16_ulps(np.array([1.0 + 2.0 ** -7]), np.array([1.0])) == pytest.approx(1.0)
+    assert bf16_ulps(np.array([9.0 + 2.0 ** -5]), np.array([9.0])) == pytest.approx(0.5)
+    assert TOL_BF16_ABS == 2e-2
