@@ -36,7 +36,7 @@ def bf16_ulps(got, ref):
     return float((np.abs(got[mask] - ref[mask]) / ulp).max()) if a.size else 0.0
 
 
-def check(name, got, ref, dtype, lse=False, out_ulp=False):
+def check(name, got, ref, dtype, lse=False, out_ulp=False, exact_ref=True):
     """Assert the tolerance for one output; returns (max_abs, rel_l2).
 
     ``out_ulp`` (bf16 sums over several heads, whose magnitude can pass 8): the
@@ -44,7 +44,8 @@ def check(name, got, ref, dtype, lse=False, out_ulp=False):
     |got - ref| <= 2e-2 + 2^-9 |ref| (half an ulp of a bf16 value is at most
     2^-9 of it); the relative-L2 bar is unchanged.  Where |ref| < 4 (half an ulp
     at most 2^-7) the plain bar |got - ref| <= 2e-2 still holds, so the relaxation
-    only serves the large values it is for."""
+    only serves the large values it is for; ``exact_ref=False`` drops that part for
+    references that carry bf16 roundings of their own (a sum of rounded outputs)."""
     got = f64(got) if isinstance(got, torch.Tensor) else got
     assert np.all(np.isfinite(got[~np.isnan(ref)])), f"{name}: non-finite output"
     max_abs, rel, ref_max = errors(got, ref)
@@ -56,11 +57,10 @@ def check(name, got, ref, dtype, lse=False, out_ulp=False):
             f"{name}: max(|err| - 2^-9 |ref|) {excess:.3e} > {TOL_BF16_ABS} (|ref| <= {ref_max:.2f}, "
             f"max-abs {max_abs:.3e} = {ulps:.1f} bf16 ulps of |ref|)")
         small = mask & (np.abs(np.where(mask, ref, 0.0)) < 4.0)
-        if small.any():
+        if exact_ref and small.any():
             small_abs = float(np.abs(got[small] - ref[small]).max())
             assert small_abs <= TOL_BF16_ABS, (
-                f"{name}: max-abs {small_abs:.3e} > {TOL_BF16_ABS} where |ref| < 4 "
-                f"({bf16_ulps(got[small], ref[small]):.1f} bf16 ulps of |ref|)")
+                f"{name}: max-abs {small_abs:.3e} > {TOL_BF16_ABS} where |ref| < 4")
         assert rel <= TOL_BF16_REL, (
             f"{name}: rel-L2 {rel:.3e} > {TOL_BF16_REL} (max-abs {max_abs:.3e} = {ulps:.1f} bf16 "
             f"ulps of |ref|)")

@@ -86,9 +86,11 @@ def test_gqa_equals_ungrouped_on_repeated_kv():
     dq2, dk2, dv2 = swattn.bwd(x["q"], rep["k"], rep["v"], o2, x["do"], lse2, W, scale)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2) and torch.equal(dq, dq2)
+    # the reference sums G per-head gradients that were each rounded to bf16 (up to half
+    # an ulp each): it carries roundings of its own, so only the rounding-aware bar applies
     for got, per_head in ((dk, dk2), (dv, dv2)):
         ref = f64(per_head).reshape(B, T, Hkv, G, D).sum(axis=3)
-        check("group sum", got, ref, torch.bfloat16, out_ulp=True)
+        check("group sum", got, ref, torch.bfloat16, out_ulp=True, exact_ref=False)
 
 
 def test_gqa_full_size_sampled():

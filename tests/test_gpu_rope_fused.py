@@ -143,5 +143,7 @@ def test_fused_equals_unfused_path():
     assert not bad.any(), (a[bad][:8].tolist(), b[bad][:8].tolist())
     for n, a, b in (("o", got["o"], o), ("lse", got["lse"], lse), ("dv", got["dv"], dv)):
         check(f"fused vs unfused {n}", a, f64(b), torch.bfloat16, lse=(n == "lse"))
+    # the unfused dq, dk are bf16 outputs themselves (rounded once more than the oracle):
+    # only the rounding-aware bar applies
     for n, a, b in (("dq", got["dq"], dq), ("dk", got["dk"], dk)):
-        check(f"fused vs unfused {n}", a, f64(b), torch.bfloat16, out_ulp=True)
+        check(f"fused vs unfused {n}", a, f64(b), torch.bfloat16, out_ulp=True, exact_ref=False)

@@ -53,3 +53,15 @@ def test_bf16_ulps():
     assert bf16_ulps(np.array([1.0 + 2.0 ** -7]), np.array([1.0])) == pytest.approx(1.0)
     assert bf16_ulps(np.array([9.0 + 2.0 ** -5]), np.array([9.0])) == pytest.approx(0.5)
     assert TOL_BF16_ABS == 2e-2
+
+
+def test_out_ulp_bar_with_a_rounded_reference():
+    """A reference that is itself a sum of rounded outputs keeps only the
+    rounding-aware bar."""
+    ref = np.full(1000, 3.0)
+    ref[0], ref[1] = 3.9, np.nan
+    got = np.where(np.isnan(ref), 0.0, ref)
+    got[0] = 3.9255  # 0.0255 - 3.9 / 512 = 0.0179 on top of the rounding
+    check("rounded ref", got, ref, BF, out_ulp=True, exact_ref=False)
+    with pytest.raises(AssertionError, match="where \\|ref\\| < 4"):
+        check("exact ref", got, ref, BF, out_ulp=True)
