@@ -16,15 +16,27 @@ constexpr int kVersion = 103;  // 0.1.3: QK-norm + rotary prologue (swattn_qk_no
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Whether the product of the (non-negative) factors is at most `limit`, decided without
+// forming a product that could overflow.
+bool product_at_most(long long limit, std::initializer_list<long long> factors) {
+  long long p = 1;
+  for (long long f : factors) {
+    if (f < 0) return false;
+    if (f != 0 && p > limit / f) return false;
+    p *= f;
+  }
+  return true;
+}
+
 int check_common(int B, int H, int T, int D, int window) {
   if (B <= 0 || H <= 0 || T <= 0 || D <= 0 || window == 0) return SWATTN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return SWATTN_ERR_UNSUPPORTED;
   // kernels index rows of [B, T, H] and grid blocks with 32-bit ints
-  const long long rows = (long long)B * T * H;
-  if (rows > INT_MAX / 2 || (long long)B * H * ((T + 127) / 128) > INT_MAX / 2)
+  if (!product_at_most(INT_MAX / 2, {B, T, H}) ||
+      !product_at_most(INT_MAX / 2, {B, H, ((long long)T + 127) / 128}))
     return SWATTN_ERR_INVALID_ARG;
   // buffer loads address one sequence's [T, H, D] block with 32-bit byte offsets
-  if ((long long)(T + 128) * H * D * 2 > INT_MAX) return SWATTN_ERR_UNSUPPORTED;
+  if (!product_at_most(INT_MAX, {(long long)T + 128, H, D, 2})) return SWATTN_ERR_UNSUPPORTED;
   return SWATTN_OK;
 }
 
@@ -59,7 +71,7 @@ int check_scale(float scale) {
 int check_decode(int B, int H, int D, int Tmax, int window) {
   if (B <= 0 || H <= 0 || D <= 0 || Tmax <= 0 || window == 0) return SWATTN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return SWATTN_ERR_UNSUPPORTED;
-  if ((long long)B * Tmax * H > INT_MAX / 2 || B > 65535 || H > 65535)
+  if (!product_at_most(INT_MAX / 2, {B, Tmax, H}) || B > 65535 || H > 65535)
     return SWATTN_ERR_INVALID_ARG;
   return SWATTN_OK;
 }
@@ -289,8 +301,9 @@ int swattn_prefill(const void *q, const void *k_new, const void *v_new, void *k_
   if (st != SWATTN_OK) return st;
   if (Tmax <= 0 || Tq > Tmax) return SWATTN_ERR_INVALID_ARG;
   // the caches: 32-bit grid/row indices and 32-bit buffer offsets per sequence
-  if ((long long)B * Tmax * Hkv > INT_MAX / 2) return SWATTN_ERR_INVALID_ARG;
-  if ((long long)(Tmax + 128) * Hkv * D * 2 > INT_MAX) return SWATTN_ERR_UNSUPPORTED;
+  if (!product_at_most(INT_MAX / 2, {B, Tmax, Hkv})) return SWATTN_ERR_INVALID_ARG;
+  if (!product_at_most(INT_MAX, {(long long)Tmax + 128, Hkv, D, 2}))
+    return SWATTN_ERR_UNSUPPORTED;
   if (!all_aligned({q, k_new, v_new, k_cache, v_cache, o}) || seqlens == nullptr)
     return SWATTN_ERR_INVALID_ARG;
   return hip_status(swattn::launch_prefill_bf16(q, k_new, v_new, k_cache, v_cache, seqlens, o,
@@ -367,12 +380,14 @@ int swattn_decode_f32(const float *q, const float *k_cache, const float *v_cache
 
 static int check_prologue(int B, int T, int H, int Hkv, int D, float base, float eps) {
   // H == 0 (keys only) or Hkv == 0 (queries only) is allowed, not both
-  if (B <= 0 || T <= 0 || H < 0 || Hkv < 0 || H + Hkv == 0 || D <= 0)
+  if (B <= 0 || T <= 0 || H < 0 || Hkv < 0 || (H == 0 && Hkv == 0) || D <= 0)
     return SWATTN_ERR_INVALID_ARG;
+  // the kernel counts the row's q and k vectors, H + Hkv, in an int
+  if ((long long)H + Hkv > INT_MAX / 2) return SWATTN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return SWATTN_ERR_UNSUPPORTED;
   if (!(base > 0.f) || !std::isfinite(base) || !(eps >= 0.f) || !std::isfinite(eps))
     return SWATTN_ERR_INVALID_ARG;
-  if ((long long)B * T > INT_MAX / 2) return SWATTN_ERR_INVALID_ARG;  // 32-bit row indices
+  if (!product_at_most(INT_MAX / 2, {B, T})) return SWATTN_ERR_INVALID_ARG;  // 32-bit row indices
   return SWATTN_OK;
 }
 

@@ -260,7 +260,8 @@ int swattn_decode_gqa(const void *q, const void *k_cache, const void *v_cache,
  * may be NULL); not both.  Outputs may be their own inputs (in place); other
  * overlaps are not allowed.
  * INVALID_ARG: a NULL or misaligned tensor of a present side, B, T <= 0, H or Hkv < 0,
- * H + Hkv == 0, base <= 0, eps < 0 or either not finite, B * T > INT_MAX / 2.
+ * H + Hkv == 0 or > INT_MAX / 2, base <= 0, eps < 0 or either not finite,
+ * B * T > INT_MAX / 2.
  * UNSUPPORTED: D not 64 or 128.  Asynchronous on `stream`; no workspace.
  */
 int swattn_qk_norm_rope(const void *q, const void *k, void *q_out, void *k_out,
