@@ -53,7 +53,12 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (AMD public spec)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (AMD public spec)
 METRIC = "attn fwd+bwd TFLOP/s (masked FLOPs) and % bf16 MFMA peak; decode HBM GB/s"
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
-KERNEL_SOURCES = sorted(glob.glob(os.path.join(ROOT, "causal_sliding_window_amd", "csrc", "*")))
+# the files that hold the kernels and their launch configurations: every source of the
+# library except the C ABI's argument checks (api.hip), the allocation-free decode's
+# scratch array (noalloc.hip) and the measurement probes (probe.hip); the counters in
+# profiles/ are keyed to a hash of these
+KERNEL_SOURCES = sorted(p for p in glob.glob(os.path.join(ROOT, "causal_sliding_window_amd", "csrc", "*"))
+                        if os.path.basename(p) not in ("api.hip", "noalloc.hip", "probe.hip"))
 
 
 def log(*a):
