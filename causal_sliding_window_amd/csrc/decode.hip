@@ -3,11 +3,12 @@
 // read).  Bound by HBM: every visible K/V cache row is read exactly once.
 //
 // decode_split_kernel: workgroup (K/V head hk, chunk c, sequence b) reads seqlens[b]
-//   on the device, takes its kDecodeChunkWide rows (8 waves of 32) of the visible range
-//   [max(0, L - W), L), and for each query head that reads K/V head hk (H / Hkv of
-//   them; one without grouping) writes a partial (o_c normalised, lse_c) to the
-//   workspace (or o and lse directly when the visible range is one chunk).  The
-//   cache rows are read once per group, not once per query head.  Each
+//   on the device, takes its chunk of the visible range [max(0, L - W), L) (32 rows per
+//   wave: kDecodeChunkWide rows in 8 waves ungrouped, kDecodeChunk in 4 grouped), and
+//   for each query head that reads K/V head hk (H / Hkv of them; one without
+//   grouping) writes a partial (o_c normalised, lse_c) to the workspace (or o and lse
+//   directly when the visible range is one chunk).  The cache rows are read once per
+//   group, not once per query head.  Each
 //   K/V row of one head is 256 contiguous bytes (bf16, D = 128) read by D/8 lanes
 //   with non-temporal 16-byte loads; every wave requests all of its rows before
 //   using any.
@@ -541,7 +542,7 @@ static hipError_t launch_decode_t(const void *q, const void *k_cache, const void
                                   int Hkv, int Tmax, int window, float scale, float *ws,
                                   hipStream_t st) {
   // the workspace holds decode_num_splits(Tmax, window) partials per (b, h): enough for
-  // the kDecodeChunk-row chunks of the matrix-core kernel; the vector split kernel takes
+  // the kDecodeChunk-row chunks of the grouped kernels; the ungrouped split kernel takes
   // chunks of kDecodeChunkWide rows, half as many
   const int ns_ws = decode_num_splits(Tmax, window);
   float *ws_o = ws;
@@ -551,22 +552,23 @@ static hipError_t launch_decode_t(const void *q, const void *k_cache, const void
     decode_gqa_mfma_kernel<<<dim3(Hkv, ns, B), 256, 0, st>>>(
         (const uint16_t *)q, (const uint16_t *)k_cache, (const uint16_t *)v_cache, seqlens, ws_o,
         ws_lse, (uint16_t *)o, lse, H, Hkv, Tmax, window, scale, ns);
+  } else if (Hkv != H) {
+    // grouped, vector ALU: kDecodeChunk-row chunks of four waves.  The group's heads
+    // are served in turn from K/V rows held in registers (172 VGPRs); with eight waves
+    // per workgroup a CU would hold one workgroup instead of two (measured: groups of
+    // two 54.0 against 70.7 us causal).
+    decode_split_kernel<TT, D, true, 4><<<dim3(Hkv, ns, B), 256, 0, st>>>(
+        (const TT *)q, (const TT *)k_cache, (const TT *)v_cache, seqlens, ws_o, ws_lse, (TT *)o,
+        lse, H, Hkv, Tmax, window, scale, ns);
   } else {
-    // the vector kernels, grouped or not, take the same kDecodeChunkWide-row chunks:
-    // one query head's arithmetic is then the same on both (at D = 64 the grouped
-    // decode of a cache equals the ungrouped decode of that cache repeated over the group)
+    // ungrouped: kDecodeChunkWide-row chunks of eight waves
     constexpr int NWW = kDecodeChunkWide / 32;
     chunk = kDecodeChunkWide;
     const int vis = window > 0 ? (window < Tmax ? window : Tmax) : Tmax;
     ns = (vis + chunk - 1) / chunk;
-    if (Hkv != H)
-      decode_split_kernel<TT, D, true, NWW><<<dim3(Hkv, ns, B), 64 * NWW, 0, st>>>(
-          (const TT *)q, (const TT *)k_cache, (const TT *)v_cache, seqlens, ws_o, ws_lse,
-          (TT *)o, lse, H, Hkv, Tmax, window, scale, ns);
-    else
-      decode_split_kernel<TT, D, false, NWW><<<dim3(Hkv, ns, B), 64 * NWW, 0, st>>>(
-          (const TT *)q, (const TT *)k_cache, (const TT *)v_cache, seqlens, ws_o, ws_lse,
-          (TT *)o, lse, H, Hkv, Tmax, window, scale, ns);
+    decode_split_kernel<TT, D, false, NWW><<<dim3(Hkv, ns, B), 64 * NWW, 0, st>>>(
+        (const TT *)q, (const TT *)k_cache, (const TT *)v_cache, seqlens, ws_o, ws_lse, (TT *)o,
+        lse, H, Hkv, Tmax, window, scale, ns);
   }
   // partials of (b, h) at slots b h ns .. + ns - 1 (ns <= ns_ws)
   if (ns > 1)

@@ -8,8 +8,8 @@
 
 namespace swattn {
 
-// Number of KV rows one decode workgroup handles (grouped kernels), and one workgroup of
-// the ungrouped split kernel (eight waves of 32 rows).
+// Number of KV rows one decode workgroup handles: grouped kernels (four waves of 32
+// rows), and the ungrouped split kernel (eight waves of 32 rows).
 constexpr int kDecodeChunk = 128;
 constexpr int kDecodeChunkWide = 256;
 // Query heads whose partials a grouped decode workgroup merges together (its LDS holds
