@@ -119,6 +119,24 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+# the source file of each measured kernel; every kernel also depends on the shared
+# device helpers and launch constants
+KERNEL_FILES = {"fwd": "fwd_bf16.hip", "bwd_dq": "bwd_bf16.hip", "bwd_dkdv": "dkdv_bf16.hip",
+                "decode_split": "decode.hip", "decode_merge": "decode.hip"}
+SHARED_FILES = ("common.h", "launch.h", "rope.h")
+
+
+def kernel_hash(kernel: str) -> str:
+    """Hash of the sources one measured kernel is built from: its counters stay valid
+    while this is unchanged."""
+    csrc = os.path.join(ROOT, "causal_sliding_window_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_FILES[kernel],) + SHARED_FILES:
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 # ----------------------------------------------------------------------------- GPU legs
 def clock_ramp(torch, fn, seconds):
     """Runs ``fn`` (one step) back to back for at least ``seconds`` of wall time, so the
@@ -702,15 +720,14 @@ def cpu_baseline(inputs, budget_s=12.0):
 # ----------------------------------------------------------------------------- counters
 def traffic_for(kernel: str):
     """HBM bytes per launch from stored rocprofv3 FETCH_SIZE/WRITE_SIZE counters, scaled by a
-    plain copy kernel's reading; None when missing or taken on different kernel sources."""
+    plain copy kernel's reading; None when missing or taken on other sources of that
+    kernel (its file or the shared headers)."""
     try:
         data = json.load(open(COUNTERS))
     except Exception:
         return None
-    if data.get("source_hash") != source_hash():
-        return None
     k = data.get("kernels", {}).get(kernel)
-    if not k:
+    if not k or k.get("sources") != kernel_hash(kernel):
         return None
     return int(k["fetch_bytes"] * data["fetch_factor"] + k["write_bytes"] * data["write_factor"])
 
@@ -748,11 +765,12 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
     for n, sub in names.items():
         f, w = pick(fe, sub), pick(wr, sub)
         if f is not None and w is not None:
-            out["kernels"][n] = {"fetch_bytes": f, "write_bytes": w}
-    try:  # instruction counters of the same sources are kept
+            out["kernels"][n] = {"fetch_bytes": f, "write_bytes": w, "sources": kernel_hash(n)}
+    try:  # instruction counters of kernels whose sources are unchanged are kept
         old = json.load(open(COUNTERS))
-        if old.get("source_hash") == out["source_hash"] and "sq" in old:
-            out["sq"] = old["sq"]
+        sq = {n: d for n, d in old.get("sq", {}).items() if d.get("sources") == kernel_hash(n)}
+        if sq:
+            out["sq"] = sq
     except Exception:
         pass
     os.makedirs(os.path.dirname(COUNTERS), exist_ok=True)
@@ -783,12 +801,15 @@ def ingest_sq(csv_paths):
                     vals.setdefault(n, {}).setdefault(r["Counter_Name"], []).append(
                         float(r["Counter_Value"]))
     out = {n: {c: statistics.fmean(v) for c, v in d.items()} for n, d in vals.items()}
+    for n, d in out.items():
+        d["sources"] = kernel_hash(n)
     try:
         data = json.load(open(COUNTERS))
     except Exception:
         data = {}
-    if data.get("source_hash") not in (None, source_hash()):
-        data = {}  # HBM counters of other sources are dropped with them
+    # HBM counters of kernels whose sources changed are dropped
+    data["kernels"] = {n: d for n, d in data.get("kernels", {}).items()
+                       if d.get("sources") == kernel_hash(n)}
     data["source_hash"] = source_hash()
     data["sq"] = out
     os.makedirs(os.path.dirname(COUNTERS), exist_ok=True)
