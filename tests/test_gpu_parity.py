@@ -265,6 +265,32 @@ def test_decode_many_heads_short_ranges(dtype, D, W, Tmax):
     check("lse", lse[1:], rl[1:], td, lse=True)
 
 
+@pytest.mark.parametrize("Hkv", [None, 4, 2])
+@pytest.mark.parametrize("W", [-1, 300])
+def test_decode_ignores_workspace_contents(Hkv, W):
+    """The workspace is filled with NaN before the call: only the partials of chunks
+    with visible rows are read by the merge, and sequences whose range is one chunk
+    (or empty) are written by the split kernels directly.  Ungrouped (256-row chunks),
+    grouped on the matrix cores (groups of 3) and on the vector ALU (groups of 6 at
+    D = 64)."""
+    lens = [0, 1, 2, 100, 255, 256, 257, 700, 1200, 1500]
+    D = 64 if Hkv == 2 else 128
+    H = 12
+    d = inputs.decode_inputs(len(lens), H, D, 1500, "bf16", seed=31 + (Hkv or 0), lengths=lens,
+                             Hkv=Hkv)
+    g = _gpu(d)
+    scale = 1 / math.sqrt(D)
+    nbytes = swattn.swattn_decode_workspace_size(len(lens), H, D, 1500, W)
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    o, lse = swattn.decode(g["q"], g["k_cache"], g["v_cache"], g["seqlens"], W, scale,
+                           workspace=ws)
+    torch.cuda.synchronize()
+    ro, rl = _decode_oracle(d, W, scale)
+    assert torch.all(o[0] == 0) and torch.all(lse[0] == -math.inf)  # the empty sequence
+    check("o", o, ro, torch.bfloat16)
+    check("lse", lse[1:], rl[1:], torch.bfloat16, lse=True)
+
+
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
 @pytest.mark.parametrize("W", [-1, 9000])
 def test_decode_long_cache(dtype, D, W):
