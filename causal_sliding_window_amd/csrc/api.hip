@@ -429,26 +429,35 @@ static swattn::RopeArgs rope_args(const int *pos_offset, int D, float base, floa
   return ra;
 }
 
-int swattn_fwd_rope(const void *q, const void *k_rope, const void *v, void *o, float *lse,
-                    void *q_rope, const int *pos_offset, int B, int H, int T, int D, int window,
-                    float scale, float base, float eps, swattn_stream_t stream) {
+int swattn_fwd_rope_gqa(const void *q, const void *k_rope, const void *v, void *o, float *lse,
+                        void *q_rope, const int *pos_offset, int B, int H, int Hkv, int T, int D,
+                        int window, float scale, float base, float eps, swattn_stream_t stream) {
   int st = check_common(B, H, T, D, window);
+  if (st == SWATTN_OK) st = check_group(H, Hkv);
   if (st == SWATTN_OK) st = check_scale(scale);
   if (st == SWATTN_OK) st = check_rope_args(base, eps);
   if (st != SWATTN_OK) return st;
   if (!all_aligned({q, k_rope, v, o}) || lse == nullptr) return SWATTN_ERR_INVALID_ARG;
   if (q_rope != nullptr && !all_aligned({q_rope})) return SWATTN_ERR_INVALID_ARG;
   const swattn::RopeArgs ra = rope_args(pos_offset, D, base, eps);
-  return hip_status(swattn::launch_fwd_bf16_rope(q, k_rope, v, o, lse, q_rope, B, H, T, D, window,
-                                                 scale, ra, (hipStream_t)stream));
+  return hip_status(swattn::launch_fwd_bf16_rope(q, k_rope, v, o, lse, q_rope, B, H, Hkv, T, D,
+                                                 window, scale, ra, (hipStream_t)stream));
 }
 
-int swattn_bwd_rope(const void *q, const void *k, const void *q_rope, const void *k_rope,
-                    const void *v, const void *o, const void *dO, const float *lse, void *dq,
-                    void *dk, void *dv, const int *pos_offset, int B, int H, int T, int D,
-                    int window, float scale, float base, float eps, void *workspace,
-                    swattn_stream_t stream) {
+int swattn_fwd_rope(const void *q, const void *k_rope, const void *v, void *o, float *lse,
+                    void *q_rope, const int *pos_offset, int B, int H, int T, int D, int window,
+                    float scale, float base, float eps, swattn_stream_t stream) {
+  return swattn_fwd_rope_gqa(q, k_rope, v, o, lse, q_rope, pos_offset, B, H, H, T, D, window,
+                             scale, base, eps, stream);
+}
+
+int swattn_bwd_rope_gqa(const void *q, const void *k, const void *q_rope, const void *k_rope,
+                        const void *v, const void *o, const void *dO, const float *lse, void *dq,
+                        void *dk, void *dv, const int *pos_offset, int B, int H, int Hkv, int T,
+                        int D, int window, float scale, float base, float eps, void *workspace,
+                        swattn_stream_t stream) {
   int s = check_common(B, H, T, D, window);
+  if (s == SWATTN_OK) s = check_group(H, Hkv);
   if (s == SWATTN_OK) s = check_scale(scale);
   if (s == SWATTN_OK) s = check_rope_args(base, eps);
   if (s != SWATTN_OK) return s;
@@ -456,14 +465,25 @@ int swattn_bwd_rope(const void *q, const void *k, const void *q_rope, const void
     return SWATTN_ERR_INVALID_ARG;
   const swattn::RopeArgs ra = rope_args(pos_offset, D, base, eps);
   float *delta = (float *)workspace;
+  float *part = (float *)((char *)workspace + delta_bytes(B, H, T));
   // dQ pass: raw q held (and transformed) in registers, transformed k streamed; dK/dV pass:
-  // raw k held, transformed q streamed
-  hipError_t e = swattn::launch_bwd_dq_bf16(q, k_rope, v, o, dO, lse, delta, dq, B, H, H, T, D,
+  // raw k held, transformed q streamed (with K/V head groups: per-query-head partials
+  // after delta in the workspace, then the group sum)
+  hipError_t e = swattn::launch_bwd_dq_bf16(q, k_rope, v, o, dO, lse, delta, dq, B, H, Hkv, T, D,
                                              window, scale, (hipStream_t)stream, &ra);
   if (e == hipSuccess)
-    e = swattn::launch_bwd_dkdv_bf16(q_rope, k, v, dO, lse, delta, dk, dv, nullptr, B, H, H, T, D,
+    e = swattn::launch_bwd_dkdv_bf16(q_rope, k, v, dO, lse, delta, dk, dv, part, B, H, Hkv, T, D,
                                      window, scale, (hipStream_t)stream, &ra);
   return hip_status(e);
+}
+
+int swattn_bwd_rope(const void *q, const void *k, const void *q_rope, const void *k_rope,
+                    const void *v, const void *o, const void *dO, const float *lse, void *dq,
+                    void *dk, void *dv, const int *pos_offset, int B, int H, int T, int D,
+                    int window, float scale, float base, float eps, void *workspace,
+                    swattn_stream_t stream) {
+  return swattn_bwd_rope_gqa(q, k, q_rope, k_rope, v, o, dO, lse, dq, dk, dv, pos_offset, B, H,
+                             H, T, D, window, scale, base, eps, workspace, stream);
 }
 
 }  // extern "C"

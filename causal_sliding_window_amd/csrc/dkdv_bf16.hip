@@ -83,7 +83,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     const float *__restrict__ lse, const float *__restrict__ delta, uint16_t *__restrict__ dk,
     uint16_t *__restrict__ dv, float *__restrict__ part_k, float *__restrict__ part_v, int B,
     int H, int Hkv, int T, int window, float scale, int nkt, RopeArgs ra = RopeArgs{}) {
-  static_assert(!(ROPE && PARTIAL), "the fused prologue serves H == Hkv only");
   using C = DkdvCfg<D>;
   // One LDS array (with a single __shared__ variable the compiler keeps the restrict
   // scopes below): [slot][Q, dO][TSZ] bf16, then [slot][VSZ] float (lse, delta,
@@ -396,7 +395,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       // dk: back through the prologue, with the raw key row read again (every lane of
       // the wave takes part: the reductions pair lanes l and l ^ 32); the key index and
       // the frequency ratio made opaque, so that nothing of the P side's prologue is
-      // held in registers through the loop for this
+      // held in registers through the loop for this.  With K/V head groups this query
+      // head's share of dk' is mapped (the map is linear in dk' for the fixed raw row,
+      // so the group sum of the mapped shares is dk) and written as an fp32 partial.
       int ki = my_k;
       RopeArgs re = ra;
       asm volatile("" : "+v"(ki), "+s"(re.ratio));
@@ -406,16 +407,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       load_acc_order<D>(kb + (size_t)min(ki, T - 1) * rsk, h, xr);
       rope_norm_grad_acc<D>(acc, xr, rope_pos(re, b, ki), ki < T, re, h);
       if (ki < T) {
-        uint16_t *ob = dk + base_kv + (size_t)ki * rsk;
+        if constexpr (PARTIAL) {
+          float *pp = part_k + base + (size_t)ki * rs;
 #pragma unroll
-        for (int d = 0; d < C::NDB; ++d)
+          for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            bf16x4 pk;
+            for (int g = 0; g < 4; ++g)
+              *reinterpret_cast<f32x4 *>(pp + 32 * d + 8 * g + 4 * h) =
+                  f32x4{acc[d][4 * g], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]};
+        } else {
+          uint16_t *ob = dk + base_kv + (size_t)ki * rsk;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pk[e] = (__bf16)acc[d][4 * g + e];
-            *reinterpret_cast<bf16x4 *>(ob + 32 * d + 8 * g + 4 * h) = pk;
-          }
+          for (int d = 0; d < C::NDB; ++d)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              bf16x4 pk;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) pk[e] = (__bf16)acc[d][4 * g + e];
+              *reinterpret_cast<bf16x4 *>(ob + 32 * d + 8 * g + 4 * h) = pk;
+            }
+        }
       }
       return;
     }
@@ -507,8 +518,7 @@ hipError_t launch_bwd_dkdv_bf16(const void *q, const void *k, const void *v, con
                                 const float *lse, const float *delta, void *dk, void *dv,
                                 float *part, int B, int H, int Hkv, int T, int D, int window,
                                 float scale, hipStream_t st, const RopeArgs *rope) {
-  if (rope != nullptr) {
-    if (Hkv != H) return hipErrorInvalidValue;  // the fused prologue serves H == Hkv only
+  if (rope != nullptr && Hkv == H) {
     if (D == 128)
       launch_dkdv_t<128, false, true>(q, k, v, dO, lse, delta, dk, dv, nullptr, nullptr, B, H, H,
                                       T, window, scale, st, *rope);
@@ -527,12 +537,20 @@ hipError_t launch_bwd_dkdv_bf16(const void *q, const void *k, const void *v, con
     return hipGetLastError();
   }
   float *part_k = part, *part_v = part + (size_t)B * T * H * D;
-  if (D == 128)
+  if (rope != nullptr) {
+    if (D == 128)
+      launch_dkdv_t<128, true, true>(q, k, v, dO, lse, delta, dk, dv, part_k, part_v, B, H, Hkv,
+                                     T, window, scale, st, *rope);
+    else
+      launch_dkdv_t<64, true, true>(q, k, v, dO, lse, delta, dk, dv, part_k, part_v, B, H, Hkv,
+                                    T, window, scale, st, *rope);
+  } else if (D == 128) {
     launch_dkdv_t<128, true>(q, k, v, dO, lse, delta, dk, dv, part_k, part_v, B, H, Hkv, T,
                              window, scale, st);
-  else
+  } else {
     launch_dkdv_t<64, true>(q, k, v, dO, lse, delta, dk, dv, part_k, part_v, B, H, Hkv, T,
                             window, scale, st);
+  }
   const long long n8 = (long long)B * T * Hkv * D / 8;
   dkdv_group_sum_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(
       part_k, part_v, (uint16_t *)dk, (uint16_t *)dv, n8, H / Hkv, D);

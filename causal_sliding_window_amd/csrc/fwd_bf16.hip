@@ -466,18 +466,18 @@ hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o,
 }
 
 hipError_t launch_fwd_bf16_rope(const void *q, const void *k, const void *v, void *o, float *lse,
-                                void *q_rope, int B, int H, int T, int D, int window, float scale,
-                                const RopeArgs &ra, hipStream_t st) {
+                                void *q_rope, int B, int H, int Hkv, int T, int D, int window,
+                                float scale, const RopeArgs &ra, hipStream_t st) {
   const int nqt = (T + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
   dim3 grid((unsigned)(nqt * B * H)), block(256);
   if (D == 128)
     fwd_bf16_kernel<128, false, true><<<grid, block, 0, st>>>(
         (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr,
-        B, H, H, T, T, window, scale, nqt, ra, (uint16_t *)q_rope);
+        B, H, Hkv, T, T, window, scale, nqt, ra, (uint16_t *)q_rope);
   else
     fwd_bf16_kernel<64, false, true><<<grid, block, 0, st>>>(
         (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr,
-        B, H, H, T, T, window, scale, nqt, ra, (uint16_t *)q_rope);
+        B, H, Hkv, T, T, window, scale, nqt, ra, (uint16_t *)q_rope);
   return hipGetLastError();
 }
 

@@ -30,10 +30,10 @@ hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o,
                            int B, int H, int Hkv, int T, int D, int window, float scale,
                            hipStream_t st);
 // Forward with the QK-norm + rotary prologue fused into the query load (q raw, k already
-// transformed; H == Hkv); q_rope (nullable) receives the transformed queries.
+// transformed); q_rope (nullable) receives the transformed queries.
 hipError_t launch_fwd_bf16_rope(const void *q, const void *k, const void *v, void *o, float *lse,
-                                void *q_rope, int B, int H, int T, int D, int window, float scale,
-                                const RopeArgs &ra, hipStream_t st);
+                                void *q_rope, int B, int H, int Hkv, int T, int D, int window,
+                                float scale, const RopeArgs &ra, hipStream_t st);
 // Chunked prefill: appends the chunk's K/V rows to the caches at seqlens[b] (clamped to
 // [0, Tmax - Tq]), then runs the forward for its Tq queries against the caches.
 hipError_t launch_prefill_bf16(const void *q, const void *k_new, const void *v_new,
@@ -58,7 +58,8 @@ hipError_t launch_bwd_dq(bool bf16, const void *q, const void *k, const void *v,
 
 hipError_t launch_bwd_pre_bf16(const void *o, const void *dO, float *delta, int B, int H, int T,
                                int D, hipStream_t st);
-// rope (non-null, H == Hkv): k raw, q transformed; dk with respect to the raw k
+// rope (non-null): k raw, q transformed; dk with respect to the raw k (with K/V head
+// groups each query head's share is mapped back before the group sum)
 hipError_t launch_bwd_dkdv_bf16(const void *q, const void *k, const void *v, const void *dO,
                                 const float *lse, const float *delta, void *dk, void *dv,
                                 float *part, int B, int H, int Hkv, int T, int D, int window,

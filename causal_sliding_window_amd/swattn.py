@@ -55,6 +55,8 @@ _SIGS = {
     "swattn_qk_norm_rope_bwd": ([_P] * 7 + [_I] * 5 + [_F, _F, _P], _I),
     "swattn_fwd_rope": ([_P] * 7 + [_I] * 5 + [_F, _F, _F, _P], _I),
     "swattn_bwd_rope": ([_P] * 12 + [_I] * 5 + [_F, _F, _F, _P, _P], _I),
+    "swattn_fwd_rope_gqa": ([_P] * 7 + [_I] * 6 + [_F, _F, _F, _P], _I),
+    "swattn_bwd_rope_gqa": ([_P] * 12 + [_I] * 6 + [_F, _F, _F, _P, _P], _I),
     "swattn_probe_mfma": ([_P, _I, _I, _P], _I),
     "swattn_probe_read": ([_P, ctypes.c_size_t, _P, _I, _P], _I),
 }
@@ -441,6 +443,52 @@ def swattn_bwd_rope(q, k, q_rope, k_rope, v, o, do, lse, dq, dk, dv, window: int
                                  _ptr(pos_offset), B, H, T, D, int(window), float(scale),
                                  float(base), float(eps), _ptr(workspace),
                                  _stream(stream, q.device)), "swattn_bwd_rope")
+
+
+def swattn_fwd_rope_gqa(q, k_rope, v, o, lse, q_rope, window: int, scale: float,
+                        pos_offset=None, base: float = 10000.0, eps: float = 1e-6, stream=None):
+    """swattn_fwd_rope with K/V head groups: k_rope, v [B,T,Hkv,D]."""
+    B, T, H, D = q.shape
+    Hkv = k_rope.shape[2]
+    _groups(H, Hkv)
+    for n, t in (("q", q), ("o", o)):
+        _dev_tensor(t, n, torch.bfloat16, (B, T, H, D))
+    for n, t in (("k_rope", k_rope), ("v", v)):
+        _dev_tensor(t, n, torch.bfloat16, (B, T, Hkv, D))
+    if q_rope is not None:
+        _dev_tensor(q_rope, "q_rope", torch.bfloat16, (B, T, H, D))
+    _dev_tensor(lse, "lse", torch.float32, (B, H, T))
+    if pos_offset is not None:
+        _dev_tensor(pos_offset, "pos_offset", torch.int32, (B,))
+    _check(lib().swattn_fwd_rope_gqa(_ptr(q), _ptr(k_rope), _ptr(v), _ptr(o), _ptr(lse),
+                                     _ptr(q_rope), _ptr(pos_offset), B, H, Hkv, T, D, int(window),
+                                     float(scale), float(base), float(eps),
+                                     _stream(stream, q.device)), "swattn_fwd_rope_gqa")
+
+
+def swattn_bwd_rope_gqa(q, k, q_rope, k_rope, v, o, do, lse, dq, dk, dv, window: int,
+                        scale: float, workspace, pos_offset=None, base: float = 10000.0,
+                        eps: float = 1e-6, stream=None):
+    """swattn_bwd_rope with K/V head groups: k, k_rope, v, dk, dv [B,T,Hkv,D]."""
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    _groups(H, Hkv)
+    for n, t in (("q", q), ("q_rope", q_rope), ("o", o), ("do", do), ("dq", dq)):
+        _dev_tensor(t, n, torch.bfloat16, (B, T, H, D))
+    for n, t in (("k", k), ("k_rope", k_rope), ("v", v), ("dk", dk), ("dv", dv)):
+        _dev_tensor(t, n, torch.bfloat16, (B, T, Hkv, D))
+    _dev_tensor(lse, "lse", torch.float32, (B, H, T))
+    if pos_offset is not None:
+        _dev_tensor(pos_offset, "pos_offset", torch.int32, (B,))
+    _dev_tensor(workspace, "workspace")
+    if workspace.numel() * workspace.element_size() < swattn_bwd_gqa_workspace_size(B, H, Hkv, T,
+                                                                                   D):
+        raise SwattnError("workspace too small")
+    _check(lib().swattn_bwd_rope_gqa(_ptr(q), _ptr(k), _ptr(q_rope), _ptr(k_rope), _ptr(v),
+                                     _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                     _ptr(pos_offset), B, H, Hkv, T, D, int(window), float(scale),
+                                     float(base), float(eps), _ptr(workspace),
+                                     _stream(stream, q.device)), "swattn_bwd_rope_gqa")
 
 
 # ----------------------------------------------------------------------------- allocating wrappers

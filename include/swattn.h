@@ -282,7 +282,7 @@ int swattn_qk_norm_rope_bwd(const void *q, const void *k, const void *dq_out,
 
 /*
  * Attention with the QK-norm + rotary prologue fused into the passes that hold q or k
- * in registers (bf16, no K/V head groups: k, v [B,T,H,D]).  Same definitions as
+ * in registers (bf16; k, v [B,T,H,D], or [B,T,Hkv,D] in the _gqa forms).  Same definitions as
  * swattn_qk_norm_rope (positions, base, eps, pos_offset) and swattn_fwd / swattn_bwd;
  * a training step through the prologue and attention becomes
  *   swattn_qk_norm_rope(NULL, k, NULL, k_rope, pos_offset, B, T, 0, H, ...)  (keys only)
@@ -305,8 +305,15 @@ int swattn_qk_norm_rope_bwd(const void *q, const void *k, const void *dq_out,
  * swattn_bwd_rope: q, k raw; q_rope, k_rope transformed; o, lse from swattn_fwd_rope;
  *   dq, dk with respect to the raw q and k, dv as swattn_bwd.  Workspace as
  *   swattn_bwd_workspace_size().
- * Errors: those of swattn_fwd / swattn_bwd, and INVALID_ARG for base <= 0, eps < 0 or
- * either not finite.
+ * swattn_fwd_rope_gqa / swattn_bwd_rope_gqa: the same with Hkv K/V heads shared by
+ *   groups of H / Hkv consecutive query heads (as swattn_fwd_gqa / swattn_bwd_gqa):
+ *   k, k_rope, v, dk, dv are [B,T,Hkv,D].  The prologue is applied per head, so the
+ *   keys-only prologue call takes Hkv heads.  In the dK/dV pass each query head's share
+ *   of dk' is mapped back through the prologue (the mapping is linear in dk') into an
+ *   fp32 partial before the group sum.  Workspace as swattn_bwd_gqa_workspace_size().
+ *   With Hkv == H they equal swattn_fwd_rope / swattn_bwd_rope.
+ * Errors: those of swattn_fwd / swattn_bwd (and of swattn_fwd_gqa / swattn_bwd_gqa for
+ * the _gqa forms), and INVALID_ARG for base <= 0, eps < 0 or either not finite.
  */
 int swattn_fwd_rope(const void *q, const void *k_rope, const void *v, void *o, float *lse,
                     void *q_rope, const int *pos_offset, int B, int H, int T, int D, int window,
@@ -316,6 +323,14 @@ int swattn_bwd_rope(const void *q, const void *k, const void *q_rope, const void
                     void *dk, void *dv, const int *pos_offset, int B, int H, int T, int D,
                     int window, float scale, float base, float eps, void *workspace,
                     swattn_stream_t stream);
+int swattn_fwd_rope_gqa(const void *q, const void *k_rope, const void *v, void *o, float *lse,
+                        void *q_rope, const int *pos_offset, int B, int H, int Hkv, int T, int D,
+                        int window, float scale, float base, float eps, swattn_stream_t stream);
+int swattn_bwd_rope_gqa(const void *q, const void *k, const void *q_rope, const void *k_rope,
+                        const void *v, const void *o, const void *dO, const float *lse, void *dq,
+                        void *dk, void *dv, const int *pos_offset, int B, int H, int Hkv, int T,
+                        int D, int window, float scale, float base, float eps, void *workspace,
+                        swattn_stream_t stream);
 
 /*
  * Measurement probes: what this GPU sustains, next to its published peaks (not part of

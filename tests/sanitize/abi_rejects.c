@@ -161,6 +161,17 @@ int main(void) {
                          inf_, F, NULL));
   REJECT(swattn_bwd_rope(F, F, F, F, F, F, F, Ff, F, F, F, Fi, 1, 2, 8, 64, -1, 1.f, 1e4f,
                          1e-6f, NULL, NULL));
+  REJECT(swattn_fwd_rope_gqa(F, F, F, F, Ff, F, Fi, 1, 6, 4, 8, 64, -1, 1.f, 1e4f, 1e-6f, NULL));
+  REJECT(swattn_fwd_rope_gqa(F, F, F, F, Ff, F, Fi, 1, 6, 0, 8, 64, -1, 1.f, 1e4f, 1e-6f, NULL));
+  REJECT(swattn_fwd_rope_gqa(F, F, F, F, Ff, F, Fi, 1, 6, 3, 8, 64, -1, 1.f, -1.f, 1e-6f, NULL));
+  REJECT(swattn_fwd_rope_gqa(F, F, F, F, Ff, F, Fi, big, big, big, big, 128, -1, 1.f, 1e4f,
+                             1e-6f, NULL));
+  REJECT(swattn_bwd_rope_gqa(F, F, F, F, F, F, F, Ff, F, F, F, Fi, 1, 6, 5, 8, 64, -1, 1.f,
+                             1e4f, 1e-6f, F, NULL));
+  REJECT(swattn_bwd_rope_gqa(F, F, F, F, F, F, F, Ff, F, F, F, Fi, 1, 6, 3, 8, 64, -1, 1.f,
+                             1e4f, nan_, F, NULL));
+  REJECT(swattn_bwd_rope_gqa(F, F, F, F, F, F, F, Ff, F, F, F, Fi, 1, 6, 3, 8, 64, -1, 1.f,
+                             1e4f, 1e-6f, NULL, NULL));
 
   /* measurement probes */
   REJECT(swattn_probe_mfma(NULL, 1, 1, NULL));

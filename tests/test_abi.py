@@ -209,6 +209,21 @@ def test_fused_rope_argument_errors():
     assert lib.swattn_bwd_rope(*p11, None, 1, 2, 8, 64, -1, 0.1, float("nan"), 1e-6, FAKE,
                                None) == 1
     assert lib.swattn_bwd_rope(*p11, None, 1, 2, 8, 64, -1, 0.1, 1e4, 1e-6, None, None) == 1
+    # the _gqa forms: Hkv after H, checked like swattn_fwd_gqa / swattn_bwd_gqa
+    assert lib.swattn_fwd_rope_gqa(*p5, None, None, 1, 6, 4, 8, 64, -1, 0.1, 1e4, 1e-6,
+                                   None) == 1
+    assert lib.swattn_fwd_rope_gqa(*p5, None, None, 1, 6, 0, 8, 64, -1, 0.1, 1e4, 1e-6,
+                                   None) == 1
+    assert lib.swattn_fwd_rope_gqa(*p5, None, None, 1, 6, 3, 8, 96, -1, 0.1, 1e4, 1e-6,
+                                   None) == 2
+    assert lib.swattn_fwd_rope_gqa(*p5, None, None, 1, 6, 3, 8, 64, -1, 0.1, 1e4, float("inf"),
+                                   None) == 1
+    assert lib.swattn_bwd_rope_gqa(*p11, None, 1, 6, 5, 8, 64, -1, 0.1, 1e4, 1e-6, FAKE,
+                                   None) == 1
+    assert lib.swattn_bwd_rope_gqa(*p11, None, 1, 6, 3, 8, 64, -1, 0.1, 0.0, 1e-6, FAKE,
+                                   None) == 1
+    assert lib.swattn_bwd_rope_gqa(*p11, None, 1, 6, 3, 8, 64, -1, 0.1, 1e4, 1e-6, None,
+                                   None) == 1
 
 
 def test_probe_argument_errors():

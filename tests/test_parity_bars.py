@@ -65,3 +65,21 @@ def test_out_ulp_bar_with_a_rounded_reference():
     check("rounded ref", got, ref, BF, out_ulp=True, exact_ref=False)
     with pytest.raises(AssertionError, match="where \\|ref\\| < 4"):
         check("exact ref", got, ref, BF, out_ulp=True)
+
+
+def test_out_ulp_bar_with_a_gain():
+    """A gradient mapped through a map of gain g: the 2e-2 parts of the bar scale by g
+    per element, the output's rounding part does not."""
+    ref = np.full(1000, 2.0)
+    ref[1] = np.nan
+    got = np.where(np.isnan(ref), 0.0, ref)
+    got[0] = 2.035  # 0.035 > 2e-2, but within 2e-2 * 1.8
+    gain = np.ones_like(ref)
+    gain[0] = 1.8
+    check("gain", got, ref, BF, out_ulp=True, gain=gain)
+    with pytest.raises(AssertionError, match="over the gain"):
+        check("gain", got, ref, BF, out_ulp=True, gain=np.where(gain > 1, 1.7, 1.0))
+    with pytest.raises(AssertionError, match="2\\^-9"):
+        check("no gain", got, ref, BF, out_ulp=True)
+    with pytest.raises(AssertionError, match="gain below 1"):
+        check("gain", got, ref, BF, out_ulp=True, gain=np.full_like(ref, 0.5))
