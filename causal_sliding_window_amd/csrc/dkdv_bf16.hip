@@ -4,17 +4,16 @@
 // nanochat guide's section 5, with P recomputed from the stored LSE:
 //   dV = P^T dO,  dK = scale * dS^T Q,  dS = P * (dP - delta),  dP = dO V^T.
 //
-// One workgroup = 4 waves x 32 keys of one (b, h).  Each wave keeps its K and V
-// rows in registers as MFMA B operands; S = Q K^T and dP = dO V^T are formed with
-// one key per lane, so P and dS feed dV^T = dO^T P and dK^T = Q^T dS as B
-// operands straight from registers; dO^T and Q^T come from transposed LDS reads.
-// Query tiles of 32 rows reach LDS by direct buffer -> LDS copies (four slots,
-// issued three tiles ahead, each step waiting only for the tile it needs next);
-// each step overlaps the S / dP MFMAs of the next tile with the gradient-side ALU
-// work of the current one.
+// One workgroup = 32 keys x NG key groups of one (b, h), each group served by two
+// waves in two roles (see bwd_dkdv_bf16_kernel): one keeps its K rows in registers
+// and forms S = Q K^T, P and dV, the other keeps its V rows and forms dP = dO V^T, dS
+// and dK.  S and dP are formed with one key per lane, so P and dS feed dV^T = dO^T P
+// and dK^T = Q^T dS as B operands straight from registers; dO^T and Q^T come from
+// transposed LDS reads.  Query tiles of 32 rows reach LDS by direct buffer -> LDS
+// copies, two steps ahead; one workgroup barrier per step.
 //
-// Built without -amdgpu-mfma-vgpr-form: the dK / dV accumulators stay in AGPRs,
-// which leaves the arch VGPRs to the operands.
+// Built with -amdgpu-mfma-vgpr-form like the other kernels: all MFMA results are in
+// arch VGPRs (the build reports no AGPRs).
 #include <type_traits>
 
 #include "common.h"
@@ -24,12 +23,17 @@
 namespace swattn {
 
 // ---------------------------------------------------------------- dK, dV
-template <int D>
+// NG key groups of 32 keys per workgroup: 4 (128 keys, eight waves, one workgroup per
+// CU) or 2 (64 keys, four waves, two workgroups per CU; for short windows, where a
+// workgroup's query range is mostly the window and a wide key block leaves each group
+// idle through the others' tiles).
+template <int D, int NG = 4>
 struct DkdvCfg {
-  static constexpr int BK = 128;          // keys per workgroup (4 key groups x 32)
+  static constexpr int BK = 32 * NG;      // keys per workgroup
   static constexpr int BQ = 32;           // queries per tile
-  static constexpr int NW = 8;            // waves: 4 P side + 4 dS side
-  static constexpr int NSLOT = 4;         // LDS tile slots (tile t in slot t % 4)
+  static constexpr int NW = 2 * NG;       // waves: NG P side + NG dS side
+  static constexpr int NSLOT = 4;         // LDS slots of Q tiles (tile t in slot t % 4)
+  static constexpr int NSLOT_O = NG == 4 ? 4 : 3;  // slots of dO tiles and lse / delta
   static constexpr int AHEAD = 2;         // tiles are copied this many steps ahead
   static constexpr int TSZ = BQ * D;      // elements of one Q (or dO) tile
   static constexpr int NDB = D / 32;
@@ -41,6 +45,11 @@ struct DkdvCfg {
   static constexpr int VSZ = NW * 64;          // floats of lse / delta (and spares) per slot
   static constexpr int XSZ = 16 * 64;          // floats of one handed-over P tile
   static_assert(CPW >= 1 && (2 * HALF) % NW == 0, "whole 1-KB pieces per wave");
+  static_assert(NG == 2 || NG == 4, "two or four key groups");
+  // bytes of LDS; with NG = 2 two workgroups share a CU's 160 KB
+  static constexpr int LDS_BYTES =
+      (NSLOT + NSLOT_O) * TSZ * 2 + NSLOT_O * VSZ * 4 + NG * 2 * XSZ * 4;
+  static_assert(NG == 4 || LDS_BYTES <= 80 * 1024, "two workgroups per CU");
 };
 
 // Largest P of a tile (any lane) from which P enters dV as bf16 hi + lo.
@@ -56,13 +65,13 @@ constexpr bool kDsLoK = D == 64;
 template <int N>
 constexpr int kWaitVmLgkm0 = (N & 15) | ((N >> 4) << 14) | (7 << 4);
 
-// One workgroup = 8 waves = 128 keys of one (b, h), in 4 groups of 32 keys; each group
-// is served by two waves with the same keys (one per role), and the two run on the
-// same SIMD (waves g and g + 4):
-//   P side  (waves 0..3): S' = Q K^T - lse / scale, P = exp2(c S'), dV^T += dO^T P;
-//                         hands P (fp32) to its partner through LDS;
-//   dS side (waves 4..7): dP' = dO V^T - delta, and one step later, with the partner's
-//                         P of that tile, dS = P dP' and dK^T += Q^T dS.
+// One workgroup = 2 NG waves = 32 NG keys of one (b, h), in NG groups of 32 keys; each
+// group is served by two waves with the same keys (one per role); with NG = 4 the two
+// run on the same SIMD (waves g and g + 4):
+//   P side  (waves 0..NG-1):   S' = Q K^T - lse / scale, P = exp2(c S'), dV^T += dO^T P;
+//                              hands P (fp32) to its partner through LDS;
+//   dS side (waves NG..2NG-1): dP' = dO V^T - delta, and one step later, with the
+//                              partner's P of that tile, dS = P dP' and dK^T += Q^T dS.
 // Each wave holds one 32-key accumulator set (dV or dK, 64 registers) and one set of
 // stationary operands (K or V rows), so two waves fit one SIMD and each covers the
 // other's waits.  Query tiles of 32 rows reach LDS by direct buffer -> LDS copies,
@@ -72,26 +81,28 @@ constexpr int kWaitVmLgkm0 = (N & 15) | ((N >> 4) << 14) | (7 << 4);
 // the G = H / Hkv that read K/V head h / G; it writes its fp32 contributions to dK
 // (already scaled) and dV to part_k / part_v, [B, T, H, D], and dkdv_group_sum_kernel
 // adds the G of each K/V head.  Otherwise dk and dv are written directly.
-// ROPE (no K/V head groups): k holds the raw keys (q the transformed queries); each key
-// row is normalised and rotated (QK norm + rotary embedding) as the P side loads it, and
-// dk is the gradient with respect to the raw key: the dS side's epilogue maps dL/dk'
-// back through the prologue.
-template <int D, bool PARTIAL, bool ROPE = false>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
+// ROPE: k holds the raw keys (q the transformed queries); each key row is normalised and
+// rotated (QK norm + rotary embedding) as the P side loads it, and dk is the gradient
+// with respect to the raw key: the dS side's epilogue maps dL/dk' back through the
+// prologue.  With PARTIAL it maps the query head's share (the map is linear in dL/dk')
+// and writes it to part_k in fp32; the group sum then adds mapped shares.
+template <int D, bool PARTIAL, bool ROPE = false, int NG = 4>
+__global__ __launch_bounds__(128 * NG, 4 / NG) void bwd_dkdv_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, uint16_t *__restrict__ dk,
     uint16_t *__restrict__ dv, float *__restrict__ part_k, float *__restrict__ part_v, int B,
     int H, int Hkv, int T, int window, float scale, int nkt, RopeArgs ra = RopeArgs{}) {
-  using C = DkdvCfg<D>;
+  using C = DkdvCfg<D, NG>;
   // One LDS array (with a single __shared__ variable the compiler keeps the restrict
-  // scopes below): [slot][Q, dO][TSZ] bf16, then [slot][VSZ] float (lse, delta,
-  // spares), then [key group][2][XSZ] float (the handed-over P tiles).
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[C::NSLOT * 2 * C::TSZ +
-                                                          C::NSLOT * C::VSZ * 2 +
-                                                          4 * 2 * C::XSZ * 2];
-  float *const vec = reinterpret_cast<float *>(smem + C::NSLOT * 2 * C::TSZ);
-  float *const xp = vec + C::NSLOT * C::VSZ;
+  // scopes below): [NSLOT][TSZ] bf16 (Q tiles), [NSLOT_O][TSZ] bf16 (dO tiles), then
+  // [NSLOT_O][VSZ] float (lse, delta, spares), then [key group][2][XSZ] float (the
+  // handed-over P tiles).  Q of tile qt - 1 is read in step qt (dK); dO is not, so dO
+  // and lse / delta need one slot fewer.
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[C::LDS_BYTES / 2];
+  uint16_t *const osm = smem + C::NSLOT * C::TSZ;
+  float *const vec = reinterpret_cast<float *>(osm + C::NSLOT_O * C::TSZ);
+  float *const xp = vec + C::NSLOT_O * C::VSZ;
 
   const int BH = B * H;
   const int bid = blockIdx.x;
@@ -109,8 +120,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in an SGPR
-  const int grp = w & 3;                                   // key group
-  const bool pside = w < 4;                                // role
+  const int grp = w & (NG - 1);                            // key group
+  const bool pside = w < NG;                               // role
   const int h = lane >> 5, ln = lane & 31;
   const int kw0 = k0 + 32 * grp;
   const int my_k = kw0 + ln;
@@ -150,26 +161,30 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   const int my_tensor = (w * C::CPW) / C::HALF;  // every copy of a wave is Q (0) or dO (1)
   const __amdgpu_buffer_rsrc_t rsrc_t = make_rsrc(my_tensor ? gb : qb, (uint32_t)T * rs * 2);
   const __amdgpu_buffer_rsrc_t rsrc_v = make_rsrc((w & 1) ? delb : lseb, (uint32_t)T * 4);
+  // tile: this wave's destination (the Q or the dO tile of the slot, by my_tensor)
   auto issue_to = [&](int qt, uint16_t *tile, float *vdst) {
     const uint32_t roff = (uint32_t)(qt * C::BQ) * (uint32_t)rs * 2;
 #pragma unroll
     for (int cc = 0; cc < C::CPW; ++cc) {
       const int jj = (w * C::CPW + cc) % C::HALF;
       const int db = jj / C::RG, row16 = 16 * (jj % C::RG);
-      buf_copy16_to_lds(rsrc_t, tile + my_tensor * C::TSZ + db * (C::BQ * 32) + row16 * 32,
+      buf_copy16_to_lds(rsrc_t, tile + db * (C::BQ * 32) + row16 * 32,
                         lane_off + (uint32_t)(row16 * rs + 32 * db) * 2 + roff);
     }
     // every wave issues exactly NCOPY copies per tile (lse by even waves, delta by odd
-    // ones, each into its own 64 floats; waves 2..7 fill spares), so the end-of-step
-    // wait can count them
+    // ones, each into its own 64 floats; waves 2 .. NW-1 fill spares), so the
+    // end-of-step wait can count them
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc_v, (__attribute__((address_space(3))) void *)(vdst + w * 64), 4,
         (uint32_t)(lane + qt * C::BQ) * 4, 0, 0, 0);
   };
-  auto q_tile = [&](int qt) { return smem + 2 * (qt & (C::NSLOT - 1)) * C::TSZ; };
-  auto vec_of = [&](int qt) { return vec + (qt & (C::NSLOT - 1)) * C::VSZ; };
+  // qt >= 0 wherever a dO slot is taken (qt - 1 only indexes Q tiles)
+  auto q_tile = [&](int qt) { return smem + (qt & (C::NSLOT - 1)) * C::TSZ; };
+  auto o_tile = [&](int qt) { return osm + ((unsigned)qt % C::NSLOT_O) * C::TSZ; };
+  auto vec_of = [&](int qt) { return vec + ((unsigned)qt % C::NSLOT_O) * C::VSZ; };
   auto xp_of = [&](int qt) { return xp + (2 * grp + (qt & 1)) * C::XSZ; };
-  auto issue = [&](int qt) { issue_to(qt, q_tile(qt), vec_of(qt)); };
+  auto dst_of = [&](int qt) { return my_tensor ? o_tile(qt) : q_tile(qt); };
+  auto issue = [&](int qt) { issue_to(qt, dst_of(qt), vec_of(qt)); };
 
   // lse and delta enter S and dP through one extra MFMA each.  MFMA row m of a tile
   // is query swap23(m); lane m of half 0 reads that query's lse, lane m of half 1
@@ -228,12 +243,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   // |dV| >= 4 outside 2e-2 of the exact gradient; below kLoP the rounding of P
   // (<= 2^-13 absolute) is far inside it.
   auto p_side = [&](bool masked, int qt, const uint16_t *__restrict__ cur,
-                    const float *__restrict__ vt, float *__restrict__ xw)
-                    __attribute__((always_inline)) {
+                    const uint16_t *__restrict__ curo, const float *__restrict__ vt,
+                    float *__restrict__ xw) __attribute__((always_inline)) {
     f32x16 s;
     sdp(cur, vt, s);
     TrOps op;
-    tr_ops(cur + C::TSZ, op);  // dO^T, read while P is formed
+    tr_ops(curo, op);  // dO^T, read while P is formed
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = fast_exp2(s[i] * c);
     // the element mask only changes P: the products below are the same code either way
@@ -246,7 +261,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     float pm = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; i += 2) pm = fmaxf(pm, fmaxf(s[i], s[i + 1]));
-    // the partner lane (same lane of wave w + 4) reads these 16 values
+    // the partner lane (same lane of wave w + NG) reads these 16 values
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4)
       reinterpret_cast<f32x4 *>(xw)[64 * c4 + lane] =
@@ -283,7 +298,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   // dS side, tile qt - 1 (when DK): dS = P dP' with the partner's P, dK^T += Q^T dS; and
   // tile qt (when DP): dP' into dpn.  dS enters dK as one bf16 unless some |dS| of the
   // wave's tile reaches kLoDsK (D = 64): then also its remainder, rounded to bf16.
-  auto ds_side = [&](bool do_dk, bool do_dp, const uint16_t *__restrict__ cur,
+  auto ds_side = [&](bool do_dk, bool do_dp, const uint16_t *__restrict__ curo,
                      const float *__restrict__ vt, const uint16_t *__restrict__ prev,
                      const float *__restrict__ xr, f32x16 &dpp, f32x16 &dpn)
                      __attribute__((always_inline)) {
@@ -319,7 +334,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (do_dp) sdp(cur + C::TSZ, vt, dpn);
+    if (do_dp) sdp(curo, vt, dpn);
   };
 
   // Step qt: the copies of tile qt + AHEAD start (every step, also past the workgroup's
@@ -336,20 +351,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0<C::NCOPY>);
     lds_barrier();
   };
-  auto p_step = [&](int qt, const uint16_t *__restrict__ cur, const float *__restrict__ vt,
-                    float *__restrict__ xw, uint16_t *__restrict__ dma,
-                    float *__restrict__ vdma) __attribute__((always_inline)) {
+  auto p_step = [&](int qt, const uint16_t *__restrict__ cur, const uint16_t *__restrict__ curo,
+                    const float *__restrict__ vt, float *__restrict__ xw,
+                    uint16_t *__restrict__ dma, float *__restrict__ vdma)
+                    __attribute__((always_inline)) {
     issue_to(qt + C::AHEAD, dma, vdma);
-    if (qt >= wqt0 && qt <= wqt1) p_side(qt == wqt0 || qt >= mlo, qt, cur, vt, xw);
+    if (qt >= wqt0 && qt <= wqt1) p_side(qt == wqt0 || qt >= mlo, qt, cur, curo, vt, xw);
     end_step();
   };
-  auto ds_step = [&](int qt, const uint16_t *__restrict__ cur, const float *__restrict__ vt,
+  auto ds_step = [&](int qt, const uint16_t *__restrict__ curo, const float *__restrict__ vt,
                      const uint16_t *__restrict__ prev, const float *__restrict__ xr,
                      uint16_t *__restrict__ dma, float *__restrict__ vdma, f32x16 &dpp,
                      f32x16 &dpn) __attribute__((always_inline)) {
     issue_to(qt + C::AHEAD, dma, vdma);
-    ds_side(qt - 1 >= wqt0 && qt - 1 <= wqt1, qt >= wqt0 && qt <= wqt1, cur, vt, prev, xr, dpp,
-            dpn);
+    ds_side(qt - 1 >= wqt0 && qt - 1 <= wqt1, qt >= wqt0 && qt <= wqt1, curo, vt, prev, xr,
+            dpp, dpn);
     end_step();
   };
 
@@ -372,20 +388,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   // steps qt0 .. qt1 + 1 (the dS side's dK trails its dP by one step)
   if (pside) {
     for (int qt = qt0; qt <= qt1 + 1; ++qt)
-      p_step(qt, q_tile(qt), vec_of(qt), xp_of(qt), q_tile(qt + C::AHEAD),
+      p_step(qt, q_tile(qt), o_tile(qt), vec_of(qt), xp_of(qt), dst_of(qt + C::AHEAD),
              vec_of(qt + C::AHEAD));
   } else {
     f32x16 dpa = f32x16{}, dpb = f32x16{};
     int qt = qt0;
     // two steps per iteration: dP' alternates between dpa and dpb
     for (; qt + 1 <= qt1 + 1; qt += 2) {
-      ds_step(qt, q_tile(qt), vec_of(qt), q_tile(qt - 1), xp_of(qt - 1), q_tile(qt + C::AHEAD),
+      ds_step(qt, o_tile(qt), vec_of(qt), q_tile(qt - 1), xp_of(qt - 1), dst_of(qt + C::AHEAD),
               vec_of(qt + C::AHEAD), dpa, dpb);
-      ds_step(qt + 1, q_tile(qt + 1), vec_of(qt + 1), q_tile(qt), xp_of(qt),
-              q_tile(qt + 1 + C::AHEAD), vec_of(qt + 1 + C::AHEAD), dpb, dpa);
+      ds_step(qt + 1, o_tile(qt + 1), vec_of(qt + 1), q_tile(qt), xp_of(qt),
+              dst_of(qt + 1 + C::AHEAD), vec_of(qt + 1 + C::AHEAD), dpb, dpa);
     }
     if (qt == qt1 + 1)
-      ds_step(qt, q_tile(qt), vec_of(qt), q_tile(qt - 1), xp_of(qt - 1), q_tile(qt + C::AHEAD),
+      ds_step(qt, o_tile(qt), vec_of(qt), q_tile(qt - 1), xp_of(qt - 1), dst_of(qt + C::AHEAD),
               vec_of(qt + C::AHEAD), dpa, dpb);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm<0>);  // no copy into LDS outlives the workgroup
@@ -502,16 +518,37 @@ __global__ __launch_bounds__(256) void dkdv_group_sum_kernel(const float *__rest
   *reinterpret_cast<bf16x4 *>(dv + e + 4) = b1;
 }
 
+// Windows up to this many keys (and shorter than the sequence) take two key groups per
+// workgroup: a 128-key block under a window W walks (W + 127) / 32 query tiles while
+// each of its groups works on (W + 31) / 32 of them, and the two waves of a group share
+// a SIMD, so that SIMD idles through the rest; two 64-key workgroups per CU cover each
+// other's idle steps and prologues.
+constexpr int kDkdvShortWindow = 512;
+
+template <int D, bool PARTIAL, bool ROPE, int NG>
+static void launch_dkdv_ng(const void *q, const void *k, const void *v, const void *dO,
+                           const float *lse, const float *delta, void *dk, void *dv,
+                           float *part_k, float *part_v, int B, int H, int Hkv, int T,
+                           int window, float scale, hipStream_t st, const RopeArgs &ra) {
+  using C = DkdvCfg<D, NG>;
+  const int nkt = (T + C::BK - 1) / C::BK;
+  const unsigned nb = (unsigned)(nkt * B * H);
+  bwd_dkdv_bf16_kernel<D, PARTIAL, ROPE, NG><<<nb, C::NW * 64, 0, st>>>(
+      (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dO, lse,
+      delta, (uint16_t *)dk, (uint16_t *)dv, part_k, part_v, B, H, Hkv, T, window, scale, nkt, ra);
+}
+
 template <int D, bool PARTIAL, bool ROPE = false>
 static void launch_dkdv_t(const void *q, const void *k, const void *v, const void *dO,
                           const float *lse, const float *delta, void *dk, void *dv,
                           float *part_k, float *part_v, int B, int H, int Hkv, int T, int window,
                           float scale, hipStream_t st, const RopeArgs &ra = RopeArgs{}) {
-  const int nkt = (T + DkdvCfg<D>::BK - 1) / DkdvCfg<D>::BK;
-  const unsigned nb = (unsigned)(nkt * B * H);
-  bwd_dkdv_bf16_kernel<D, PARTIAL, ROPE><<<nb, DkdvCfg<D>::NW * 64, 0, st>>>(
-      (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dO, lse,
-      delta, (uint16_t *)dk, (uint16_t *)dv, part_k, part_v, B, H, Hkv, T, window, scale, nkt, ra);
+  if (window > 0 && window <= kDkdvShortWindow && window < T)
+    launch_dkdv_ng<D, PARTIAL, ROPE, 2>(q, k, v, dO, lse, delta, dk, dv, part_k, part_v, B, H,
+                                        Hkv, T, window, scale, st, ra);
+  else
+    launch_dkdv_ng<D, PARTIAL, ROPE, 4>(q, k, v, dO, lse, delta, dk, dv, part_k, part_v, B, H,
+                                        Hkv, T, window, scale, st, ra);
 }
 
 hipError_t launch_bwd_dkdv_bf16(const void *q, const void *k, const void *v, const void *dO,
