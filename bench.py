@@ -780,8 +780,9 @@ def ingest_counters(fetch_csv, write_csv, copy_bytes):
 
 # the training kernels of the small workload (not the grouped, prefill, fused-prologue or
 # short-window instantiations, which the same runs may launch), matched by name prefix
-SQ_NAMES = {"fwd": "fwd_bf16_kernel<128, false, false", "bwd_dq": "bwd_dq_bf16_kernel<128, false>",
-            "bwd_dkdv": "bwd_dkdv_bf16_kernel<128, false, false>",
+SQ_NAMES = {"fwd": "fwd_bf16_kernel<128, false, false, 4>",
+            "bwd_dq": "bwd_dq_bf16_kernel<128, false>",
+            "bwd_dkdv": "bwd_dkdv_bf16_kernel<128, false, false, 4>",
             "decode_split": "decode_split_kernel<unsigned short, 128, false, ",
             "decode_merge": "decode_merge_kernel<unsigned short, 128>"}
 
