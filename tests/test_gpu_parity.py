@@ -148,6 +148,19 @@ def test_bf16_attention_sink():
     compare_all(*run_entry_points(x, -1, scale), torch.bfloat16)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("W", [511, 512, 513, 1000])
+def test_window_around_the_short_window_forms(W, D):
+    """Windows up to 512 keys (and shorter than T) take the short-window kernel forms
+    (two-wave forward workgroups, two key groups per dK/dV workgroup); 513 and 1000 take
+    the four-wave / four-group forms with a band edge inside the sequence.  Forward
+    then backward on the forward's own o and LSE, against the exact gradient."""
+    x = inputs.training_inputs(1, 1100, 2, D, "bf16", seed=W + D, qk_norm=True)
+    scale = 1 / math.sqrt(D)
+    compare_all(run_fwd_bwd(_gpu(x), W, scale), oracle_fwd_bwd(x, W, scale), torch.bfloat16,
+                tag=f"W{W} D{D} ")
+
+
 def test_long_sequence_sampled():
     """T = 8192, one head, full causal and a 512 window (largest shape tested)."""
     x = inputs.training_inputs(1, 8192, 1, 128, "bf16", seed=3, qk_norm=True)
