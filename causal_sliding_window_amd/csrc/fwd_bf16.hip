@@ -465,19 +465,31 @@ hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o,
   return hipGetLastError();
 }
 
+template <int D, int NW>
+static void launch_fwd_rope_t(const void *q, const void *k, const void *v, void *o, float *lse,
+                              void *q_rope, int B, int H, int Hkv, int T, int window,
+                              float scale, const RopeArgs &ra, hipStream_t st) {
+  const int nqt = (T + FwdCfg<D, NW>::BM - 1) / FwdCfg<D, NW>::BM;
+  fwd_bf16_kernel<D, false, true, NW><<<dim3((unsigned)(nqt * B * H)), dim3(64 * NW), 0, st>>>(
+      (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr,
+      B, H, Hkv, T, T, window, scale, nqt, ra, (uint16_t *)q_rope);
+}
+
 hipError_t launch_fwd_bf16_rope(const void *q, const void *k, const void *v, void *o, float *lse,
                                 void *q_rope, int B, int H, int Hkv, int T, int D, int window,
                                 float scale, const RopeArgs &ra, hipStream_t st) {
-  const int nqt = (T + FwdCfg<128>::BM - 1) / FwdCfg<128>::BM;
-  dim3 grid((unsigned)(nqt * B * H)), block(256);
-  if (D == 128)
-    fwd_bf16_kernel<128, false, true><<<grid, block, 0, st>>>(
-        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr,
-        B, H, Hkv, T, T, window, scale, nqt, ra, (uint16_t *)q_rope);
-  else
-    fwd_bf16_kernel<64, false, true><<<grid, block, 0, st>>>(
-        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr,
-        B, H, Hkv, T, T, window, scale, nqt, ra, (uint16_t *)q_rope);
+  const bool short_w = window > 0 && window <= kShortWindow && window < T;
+  if (D == 128) {
+    if (short_w)
+      launch_fwd_rope_t<128, 2>(q, k, v, o, lse, q_rope, B, H, Hkv, T, window, scale, ra, st);
+    else
+      launch_fwd_rope_t<128, 4>(q, k, v, o, lse, q_rope, B, H, Hkv, T, window, scale, ra, st);
+  } else {
+    if (short_w)
+      launch_fwd_rope_t<64, 2>(q, k, v, o, lse, q_rope, B, H, Hkv, T, window, scale, ra, st);
+    else
+      launch_fwd_rope_t<64, 4>(q, k, v, o, lse, q_rope, B, H, Hkv, T, window, scale, ra, st);
+  }
   return hipGetLastError();
 }
 
