@@ -385,18 +385,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     load_acc_order<D>(qb + (size_t)min(qi, T - 1) * rs, h, xr);
     rope_norm_grad_acc<D>(acc, xr, rope_pos(re, b, qi), qi < T, re, h);
   }
-  if (my_q < T) {
-    uint16_t *dqr = dq + base + (size_t)my_q * rs;
-#pragma unroll
-    for (int d = 0; d < C::NDB; ++d)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)acc[d][4 * g + e];
-        *reinterpret_cast<bf16x4 *>(dqr + 32 * d + 8 * g + 4 * h) = pk;
-      }
-  }
+  // dq through LDS (stage_rows_bf16), in the tile slots once every wave's copies have
+  // landed and every wave has finished its reads
+  static_assert(4 * 32 * D <= C::NSLOT * 2 * C::TSZ, "the waves' rows fit the tile slots");
+  __syncthreads();
+  uint16_t *stage = smem + w * 32 * D;
+  stage_rows_bf16<D>(stage, acc, 1.f, ln, h);
+  __syncthreads();
+  store_staged_rows<D>(stage, lane, T - qw0, dq + base + (size_t)qw0 * rs, rs);
 }
 
 hipError_t launch_bwd_pre_bf16(const void *o, const void *dO, float *delta, int B, int H, int T,

@@ -303,4 +303,41 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
+// Output rows through LDS.  In MFMA accumulator order a lane (half h, lane ln of the
+// half) holds 64 values of row ln: columns 32 d + 8 g + 4 h + e in acc[d][4 g + e].
+// Stored directly that is 16 store instructions per lane, each writing 32 separate
+// 16-byte pieces.  Instead a wave writes its 32 rows (times mul, as bf16) to its own
+// 32 * D elements of LDS, piece c of row r at position c ^ (r mod D / 8)
+// (stage_rows_bf16), and after a workgroup barrier reads them back 16 bytes per lane,
+// D / 8 consecutive lanes per row, storing whole rows: rows 0 .. nrows - 1 to
+// out + r * rs (store_staged_rows).
+template <int D>
+__device__ __forceinline__ void stage_rows_bf16(uint16_t *stage, const f32x16 (&acc)[D / 32],
+                                                float mul, int ln, int h) {
+  constexpr int CH = D / 8;
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[d][4 * g + e] * mul);
+      const int pc = 4 * d + g;  // columns 8 pc .. 8 pc + 7; this lane's half is h
+      *reinterpret_cast<bf16x4 *>(stage + ln * D + (pc ^ (ln & (CH - 1))) * 8 + 4 * h) = pk;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_staged_rows(const uint16_t *stage, int lane, int nrows,
+                                                  uint16_t *out, size_t rs) {
+  constexpr int CH = D / 8, RPI = 64 / CH;  // RPI rows per store instruction
+  const int pc = lane % CH, pr = lane / CH;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = pr + RPI * i;
+    const u32x4 val = *reinterpret_cast<const u32x4 *>(stage + r * D + (pc ^ (r & (CH - 1))) * 8);
+    if (r < nrows) *reinterpret_cast<u32x4 *>(out + (size_t)r * rs + 8 * pc) = val;
+  }
+}
+
 }  // namespace swattn

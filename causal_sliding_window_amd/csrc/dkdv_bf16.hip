@@ -406,6 +406,14 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void bwd_dkdv_bf16_kernel(
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm<0>);  // no copy into LDS outlives the workgroup
 
+  // bf16 dk, dv through LDS (stage_rows_bf16), in the tile slots once every wave's
+  // copies have landed and every wave has finished its reads; every wave of either role
+  // passes the same two barriers.  The fp32 partials are stored directly.
+  static_assert(PARTIAL || C::NW * 32 * D <= (C::NSLOT + C::NSLOT_O) * C::TSZ,
+                "the waves' rows fit the tile slots");
+  if constexpr (!PARTIAL) __syncthreads();
+  uint16_t *stage = smem + w * 32 * D;
+
   if constexpr (ROPE) {
     if (!pside) {
       // dk: back through the prologue, with the raw key row read again (every lane of
@@ -422,8 +430,8 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void bwd_dkdv_bf16_kernel(
       f32x16 xr[C::NDB];
       load_acc_order<D>(kb + (size_t)min(ki, T - 1) * rsk, h, xr);
       rope_norm_grad_acc<D>(acc, xr, rope_pos(re, b, ki), ki < T, re, h);
-      if (ki < T) {
-        if constexpr (PARTIAL) {
+      if constexpr (PARTIAL) {
+        if (ki < T) {
           float *pp = part_k + base + (size_t)ki * rs;
 #pragma unroll
           for (int d = 0; d < C::NDB; ++d)
@@ -431,26 +439,19 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void bwd_dkdv_bf16_kernel(
             for (int g = 0; g < 4; ++g)
               *reinterpret_cast<f32x4 *>(pp + 32 * d + 8 * g + 4 * h) =
                   f32x4{acc[d][4 * g], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]};
-        } else {
-          uint16_t *ob = dk + base_kv + (size_t)ki * rsk;
-#pragma unroll
-          for (int d = 0; d < C::NDB; ++d)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              bf16x4 pk;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) pk[e] = (__bf16)acc[d][4 * g + e];
-              *reinterpret_cast<bf16x4 *>(ob + 32 * d + 8 * g + 4 * h) = pk;
-            }
         }
+      } else {
+        stage_rows_bf16<D>(stage, acc, 1.f, ln, h);
+        __syncthreads();
+        store_staged_rows<D>(stage, lane, T - kw0, dk + base_kv + (size_t)kw0 * rsk, rsk);
       }
       return;
     }
   }
-  if (my_k < T) {
-    if (PARTIAL) {
+  const float mul = pside ? 1.f : scale;
+  if constexpr (PARTIAL) {
+    if (my_k < T) {
       float *pp = (pside ? part_v : part_k) + base + (size_t)my_k * rs;
-      const float mul = pside ? 1.f : scale;
 #pragma unroll
       for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
@@ -460,19 +461,12 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void bwd_dkdv_bf16_kernel(
           for (int e = 0; e < 4; ++e) a[e] = acc[d][4 * g + e] * mul;
           *reinterpret_cast<f32x4 *>(pp + 32 * d + 8 * g + 4 * h) = a;
         }
-    } else {
-      uint16_t *ob = (pside ? dv : dk) + base_kv + (size_t)my_k * rsk;
-      const float mul = pside ? 1.f : scale;
-#pragma unroll
-      for (int d = 0; d < C::NDB; ++d)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 pk;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[d][4 * g + e] * mul);
-          *reinterpret_cast<bf16x4 *>(ob + 32 * d + 8 * g + 4 * h) = pk;
-        }
     }
+  } else {
+    stage_rows_bf16<D>(stage, acc, mul, ln, h);
+    __syncthreads();
+    store_staged_rows<D>(stage, lane, T - kw0, (pside ? dv : dk) + base_kv + (size_t)kw0 * rsk,
+                         rsk);
   }
 }
 

@@ -421,39 +421,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
   }
 
   const float l_tot = xhalf_sum(l_run);
-  // o through LDS: a lane holds 64 of its query row's values (8-byte pieces all over
-  // the row), so it writes them to its wave's 32 rows in LDS, and the wave then stores
-  // whole 16-byte pieces with consecutive lanes on consecutive pieces of a row (D / 8
-  // lanes per row).  Piece c of row r sits at position c ^ (r mod D / 8).  The tile
-  // slots are free here: every copy has landed and every wave has passed the last
-  // barrier of the loop.
-  {
-    constexpr int CH = D / 8;        // 16-byte pieces per row
-    constexpr int RPI = 64 / CH;     // rows per store instruction
-    static_assert(NW * 32 * D <= 2 * 2 * C::TSZ, "the waves' rows fit the tile slots");
-    uint16_t *stage = smem + w * 32 * D;
-    const float inv = my_q < Tk ? 1.f / l_tot : 0.f;
-#pragma unroll
-    for (int d = 0; d < C::NDB; ++d)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[d][4 * g + e] * inv);
-        const int pc = 4 * d + g;  // columns 8 pc .. 8 pc + 7; this lane's half is h
-        *reinterpret_cast<bf16x4 *>(stage + ln * D + (pc ^ (ln & (CH - 1))) * 8 + 4 * h) = pk;
-      }
-    __syncthreads();
-    const int pc = lane % CH, pr = lane / CH;
-#pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int r = pr + RPI * i;
-      const u32x4 val =
-          *reinterpret_cast<const u32x4 *>(stage + r * D + (pc ^ (r & (CH - 1))) * 8);
-      const int qq = qw0 + r;
-      if (qq < Tk) *reinterpret_cast<u32x4 *>(o + base + (size_t)(qq - off) * rs + 8 * pc) = val;
-    }
-  }
+  // o through LDS (stage_rows_bf16): the tile slots are free here, since every copy
+  // has landed and every wave has passed the last barrier of the loop
+  static_assert(NW * 32 * D <= 2 * 2 * C::TSZ, "the waves' rows fit the tile slots");
+  uint16_t *stage = smem + w * 32 * D;
+  stage_rows_bf16<D>(stage, acc, my_q < Tk ? 1.f / l_tot : 0.f, ln, h);
+  __syncthreads();
+  store_staged_rows<D>(stage, lane, Tk - qw0, o + base + (size_t)(qw0 - off) * rs, rs);
   if (my_q < Tk && h == 0 && (!PREFILL || lse != nullptr))
     lse[(size_t)bh * T + (my_q - off)] = m_run * scale + logf(l_tot);
 }
