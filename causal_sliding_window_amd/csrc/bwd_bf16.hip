@@ -133,22 +133,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const float l2 = my_q < T ? lse[(size_t)bh * T + my_q] * kLog2e : INFINITY;
   // delta = dO . o of the lane's query (each half of the wave holds half of the
   // row), also published in the workspace for the dK/dV pass
-  float dl;
+  // (its o row is loaded here and used once the prologue's tile copies are issued, so
+  // that the two waits overlap)
+  u32x4 orow[C::KST];
   {
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + base, (uint32_t)T * rs * 2);
-    float part = 0.f;
 #pragma unroll
-    for (int st = 0; st < C::KST; ++st) {
-      const u32x4 ov =
+    for (int st = 0; st < C::KST; ++st)
+      orow[st] =
           __builtin_amdgcn_raw_buffer_load_b128(ro, (my_q * rs + 16 * st + 8 * h) * 2, 0, 0);
-      const u32x4 gv = __builtin_bit_cast(u32x4, gr[st]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        part += bf16_lo(ov[e]) * bf16_lo(gv[e]) + bf16_hi(ov[e]) * bf16_hi(gv[e]);
-    }
-    dl = xhalf_sum(part);
-    if (my_q < T && h == 0) delta[(size_t)bh * T + my_q] = dl;
   }
+  float dl = 0.f;  // delta of the lane's query, set in the prologue below
   const float c = scale * kLog2e;
 
   f32x16 acc[C::NDB];
@@ -316,10 +311,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     lds_barrier();
   };
 
-  // prologue: tiles kt0 .. kt0 + 2 in flight, the first two must land
+  // prologue: tiles kt0 .. kt0 + 2 in flight, the first two must land; delta while
+  // they are in flight
   issue(kt0);
   issue(kt0 + 1);
   issue(kt0 + 2);
+  {
+    float part = 0.f;
+#pragma unroll
+    for (int st = 0; st < C::KST; ++st) {
+      const u32x4 gv = __builtin_bit_cast(u32x4, gr[st]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        part += bf16_lo(orow[st][e]) * bf16_lo(gv[e]) + bf16_hi(orow[st][e]) * bf16_hi(gv[e]);
+    }
+    dl = xhalf_sum(part);
+    if (my_q < T && h == 0) delta[(size_t)bh * T + my_q] = dl;
+  }
   sync();
   f32x16 sc, dpc, sn, dpn;
   if (wkt0 == kt0) sdp(kt0, sc, dpc);
