@@ -129,7 +129,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     qr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     gr[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
   }
-  if constexpr (ROPE) rope_norm_operand<D>(qr, rope_pos(ra, b, my_q), my_q < T, ra, h);
   const float l2 = my_q < T ? lse[(size_t)bh * T + my_q] * kLog2e : INFINITY;
   // delta = dO . o of the lane's query (each half of the wave holds half of the
   // row), also published in the workspace for the dK/dV pass
@@ -311,11 +310,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     lds_barrier();
   };
 
-  // prologue: tiles kt0 .. kt0 + 2 in flight, the first two must land; delta while
-  // they are in flight
+  // prologue: tiles kt0 .. kt0 + 2 in flight, the first two must land; delta (and with
+  // ROPE the query transform) while they are in flight
   issue(kt0);
   issue(kt0 + 1);
   issue(kt0 + 2);
+  if constexpr (ROPE) rope_norm_operand<D>(qr, rope_pos(ra, b, my_q), my_q < T, ra, h);
   {
     float part = 0.f;
 #pragma unroll

@@ -369,9 +369,8 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void bwd_dkdv_bf16_kernel(
     end_step();
   };
 
-  // prologue: tiles qt0 and qt0 + 1 and the stationary rows, all awaited
-  issue(qt0);
-  issue(qt0 + 1);
+  // prologue: the stationary rows, then tiles qt0 and qt0 + 1, all awaited (with ROPE
+  // the key transform runs while the copies are in flight: the rows were issued first)
   {
     const __amdgpu_buffer_rsrc_t rkv = make_rsrc(pside ? kb : vb, (uint32_t)T * rsk * 2);
 #pragma unroll
@@ -379,10 +378,12 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void bwd_dkdv_bf16_kernel(
       kv[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                               rkv, (my_k * rsk + 16 * st + 8 * h) * 2, 0, 0));
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0<0>);
+  issue(qt0);
+  issue(qt0 + 1);
   if constexpr (ROPE) {
     if (pside) rope_norm_operand<D>(kv, rope_pos(ra, b, my_k), my_k < T, ra, h);
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0<0>);
   lds_barrier();
 
   // steps qt0 .. qt1 + 1 (the dS side's dK trails its dP by one step)

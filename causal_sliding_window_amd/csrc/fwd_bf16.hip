@@ -147,14 +147,6 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
           bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, ((my_q - off) * rs + 16 * st + 8 * h) * 2,
                                                         0, 0));
   }
-  if constexpr (ROPE) {
-    rope_norm_operand<D>(qr, rope_pos(ra, b, my_q - off), my_q < Tk, ra, h);
-    if (q_rope != nullptr && my_q < Tk) {
-      uint16_t *qo = q_rope + base + (size_t)(my_q - off) * rs + 8 * h;
-#pragma unroll
-      for (int st = 0; st < C::KST; ++st) *reinterpret_cast<bf16x8 *>(qo + 16 * st) = qr[st];
-    }
-  }
 
   // Copy j of a tile (1 KB): LDS block db = j / RG, rows 16 (j % RG) .. + 15.
   // Lane part of the source offset; this wave issues copies CPW w .. CPW w + CPW - 1.
@@ -341,10 +333,19 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     __syncthreads();
   };
 
-  // prologue: K, V of tile kt0 and K of kt0 + 1
+  // prologue: K, V of tile kt0 and K of kt0 + 1 (and with ROPE the query transform
+  // while those copies are in flight)
   issue(0, kt0, 0);
   issue(1, kt0, 0);
   if (kt0 < kt1) issue(0, kt0 + 1, 1);
+  if constexpr (ROPE) {
+    rope_norm_operand<D>(qr, rope_pos(ra, b, my_q - off), my_q < Tk, ra, h);
+    if (q_rope != nullptr && my_q < Tk) {
+      uint16_t *qo = q_rope + base + (size_t)(my_q - off) * rs + 8 * h;
+#pragma unroll
+      for (int st = 0; st < C::KST; ++st) *reinterpret_cast<bf16x8 *>(qo + 16 * st) = qr[st];
+    }
+  }
   sync();
   f32x16 sc, sn;
   if (wkt0 == kt0) qk(smem, sc);
