@@ -340,4 +340,41 @@ __device__ __forceinline__ void store_staged_rows(const uint16_t *stage, int lan
   }
 }
 
+// The same for fp32 rows, half a row at a time (32 rows x D / 2 floats of LDS per
+// wave): stage_rows_f32_half writes columns D / 2 * half .. + D / 2 - 1 (times mul),
+// 16-byte piece c of row r at position c ^ (r mod D / 8); store_staged_rows_f32_half
+// stores them to out + r * rs + D / 2 * half for rows 0 .. nrows - 1.
+template <int D>
+__device__ __forceinline__ void stage_rows_f32_half(float *stage, const f32x16 (&acc)[D / 32],
+                                                    float mul, int ln, int h, int half) {
+  constexpr int CH = D / 8;  // 16-byte pieces per half row
+#pragma unroll
+  for (int dd = 0; dd < D / 64; ++dd)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = D / 64 * half + dd;
+      f32x4 a;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = acc[d][4 * g + e] * mul;
+      const int pc = 8 * dd + 2 * g + h;  // columns 4 pc .. 4 pc + 3 of the half row
+      *reinterpret_cast<f32x4 *>(stage + ln * (D / 2) + (pc ^ (ln & (CH - 1))) * 4) = a;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_staged_rows_f32_half(const float *stage, int lane,
+                                                           int nrows, float *out, size_t rs,
+                                                           int half) {
+  constexpr int CH = D / 8, RPI = 64 / CH;  // RPI rows per store instruction
+  const int pc = lane % CH, pr = lane / CH;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = pr + RPI * i;
+    const f32x4 val =
+        *reinterpret_cast<const f32x4 *>(stage + r * (D / 2) + (pc ^ (r & (CH - 1))) * 4);
+    if (r < nrows)
+      *reinterpret_cast<f32x4 *>(out + (size_t)r * rs + D / 2 * half + 4 * pc) = val;
+  }
+}
+
 }  // namespace swattn

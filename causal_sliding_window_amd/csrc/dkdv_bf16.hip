@@ -407,13 +407,31 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void bwd_dkdv_bf16_kernel(
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm<0>);  // no copy into LDS outlives the workgroup
 
-  // bf16 dk, dv through LDS (stage_rows_bf16), in the tile slots once every wave's
-  // copies have landed and every wave has finished its reads; every wave of either role
-  // passes the same two barriers.  The fp32 partials are stored directly.
-  static_assert(PARTIAL || C::NW * 32 * D <= (C::NSLOT + C::NSLOT_O) * C::TSZ,
+  // dk, dv through LDS, in the tile slots once every wave's copies have landed and
+  // every wave has finished its reads: bf16 rows (stage_rows_bf16), or the fp32
+  // partials half a row at a time (stage_rows_f32_half; the same bytes per wave).
+  // Every wave of either role passes the same barriers.
+  static_assert(C::NW * 32 * D <= (C::NSLOT + C::NSLOT_O) * C::TSZ,
                 "the waves' rows fit the tile slots");
-  if constexpr (!PARTIAL) __syncthreads();
+  __syncthreads();
   uint16_t *stage = smem + w * 32 * D;
+  auto store_rows = [&](float mul, float *part, uint16_t *out) {
+    if constexpr (PARTIAL) {
+      float *fs = reinterpret_cast<float *>(stage);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (half) __syncthreads();  // the first half has been read back
+        stage_rows_f32_half<D>(fs, acc, mul, ln, h, half);
+        __syncthreads();
+        store_staged_rows_f32_half<D>(fs, lane, T - kw0, part + base + (size_t)kw0 * rs, rs,
+                                      half);
+      }
+    } else {
+      stage_rows_bf16<D>(stage, acc, mul, ln, h);
+      __syncthreads();
+      store_staged_rows<D>(stage, lane, T - kw0, out + base_kv + (size_t)kw0 * rsk, rsk);
+    }
+  };
 
   if constexpr (ROPE) {
     if (!pside) {
@@ -431,44 +449,11 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void bwd_dkdv_bf16_kernel(
       f32x16 xr[C::NDB];
       load_acc_order<D>(kb + (size_t)min(ki, T - 1) * rsk, h, xr);
       rope_norm_grad_acc<D>(acc, xr, rope_pos(re, b, ki), ki < T, re, h);
-      if constexpr (PARTIAL) {
-        if (ki < T) {
-          float *pp = part_k + base + (size_t)ki * rs;
-#pragma unroll
-          for (int d = 0; d < C::NDB; ++d)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-              *reinterpret_cast<f32x4 *>(pp + 32 * d + 8 * g + 4 * h) =
-                  f32x4{acc[d][4 * g], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]};
-        }
-      } else {
-        stage_rows_bf16<D>(stage, acc, 1.f, ln, h);
-        __syncthreads();
-        store_staged_rows<D>(stage, lane, T - kw0, dk + base_kv + (size_t)kw0 * rsk, rsk);
-      }
+      store_rows(1.f, part_k, dk);
       return;
     }
   }
-  const float mul = pside ? 1.f : scale;
-  if constexpr (PARTIAL) {
-    if (my_k < T) {
-      float *pp = (pside ? part_v : part_k) + base + (size_t)my_k * rs;
-#pragma unroll
-      for (int d = 0; d < C::NDB; ++d)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 a;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] = acc[d][4 * g + e] * mul;
-          *reinterpret_cast<f32x4 *>(pp + 32 * d + 8 * g + 4 * h) = a;
-        }
-    }
-  } else {
-    stage_rows_bf16<D>(stage, acc, mul, ln, h);
-    __syncthreads();
-    store_staged_rows<D>(stage, lane, T - kw0, (pside ? dv : dk) + base_kv + (size_t)kw0 * rsk,
-                         rsk);
-  }
+  store_rows(pside ? 1.f : scale, pside ? part_v : part_k, pside ? dv : dk);
 }
 
 // dk, dv [B, T, Hkv, D] (bf16) = sums of the G = H / Hkv partials [B, T, H, D] (fp32)
