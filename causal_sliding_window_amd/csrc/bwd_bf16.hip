@@ -159,8 +159,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   // row offset goes into the lane offsets, and offsets from row T on read as zero.
   const int my_tensor = (w * C::CPW) / C::HALF;  // every copy of a wave is K (0) or V (1)
   const __amdgpu_buffer_rsrc_t rsrc_t = make_rsrc(my_tensor ? vb : kb, (uint32_t)T * rsk * 2);
+  // Tiles past the workgroup's last one (issued so that every step waits for the same
+  // count) are copied from row T on: the buffer returns zeros and reads no memory.
   auto issue_to = [&](int kt, uint16_t *tile) {
-    const uint32_t roff = (uint32_t)(kt * C::BN) * (uint32_t)rsk * 2;
+    const uint32_t roff = (uint32_t)(kt <= kt1 ? kt * C::BN : T) * (uint32_t)rsk * 2;
 #pragma unroll
     for (int cc = 0; cc < C::CPW; ++cc) {
       const int jj = (w * C::CPW + cc) % C::HALF;

@@ -162,8 +162,11 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void bwd_dkdv_bf16_kernel(
   const __amdgpu_buffer_rsrc_t rsrc_t = make_rsrc(my_tensor ? gb : qb, (uint32_t)T * rs * 2);
   const __amdgpu_buffer_rsrc_t rsrc_v = make_rsrc((w & 1) ? delb : lseb, (uint32_t)T * 4);
   // tile: this wave's destination (the Q or the dO tile of the slot, by my_tensor)
+  // Tiles past the workgroup's last one (issued so that every step waits for the same
+  // count) are copied from row T on: the buffer returns zeros and reads no memory.
   auto issue_to = [&](int qt, uint16_t *tile, float *vdst) {
-    const uint32_t roff = (uint32_t)(qt * C::BQ) * (uint32_t)rs * 2;
+    const int qr0 = qt <= qt1 ? qt * C::BQ : T;
+    const uint32_t roff = (uint32_t)qr0 * (uint32_t)rs * 2;
 #pragma unroll
     for (int cc = 0; cc < C::CPW; ++cc) {
       const int jj = (w * C::CPW + cc) % C::HALF;
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(128 * NG, 4 / NG) void bwd_dkdv_bf16_kernel(
     // end-of-step wait can count them
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc_v, (__attribute__((address_space(3))) void *)(vdst + w * 64), 4,
-        (uint32_t)(lane + qt * C::BQ) * 4, 0, 0, 0);
+        (uint32_t)(lane + qr0) * 4, 0, 0, 0);
   };
   // qt >= 0 wherever a dO slot is taken (qt - 1 only indexes Q tiles)
   auto q_tile = [&](int qt) { return smem + (qt & (C::NSLOT - 1)) * C::TSZ; };
