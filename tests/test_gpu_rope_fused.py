@@ -181,7 +181,8 @@ def test_fused_equals_unfused_path():
 
 
 @pytest.mark.parametrize("H,Hkv", [(6, 2), (4, 1), (6, 3)])
-@pytest.mark.parametrize("T,D,W", [(300, 128, 100), (129, 64, -1), (257, 128, -1)])
+@pytest.mark.parametrize("T,D,W", [(300, 128, 100), (129, 64, -1), (257, 128, -1),
+                                   (257, 64, 65)])
 def test_fused_prologue_grouped_step(H, Hkv, T, D, W):
     """The _gqa forms: H query heads over Hkv K/V heads, against the composed oracle
     (its attention sums each K/V head's gradients over the group before the prologue's
