@@ -336,9 +336,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 // costs a share of two 32 x 32 x 16 products instead of a vector-ALU dot product per
 // query head.  Workgroup (hk, chunk c, b), four waves; wave w holds rows 32w ..
 // 32w + 31 of the chunk's kDecodeChunk rows.
-//   1. S^T (rows x heads) = K Q^T: K rows straight from HBM into A operands (tile
-//      row swap23(m) in operand row m), q of up to 32 heads as B operands; V rows
-//      copied into an LDS tile meanwhile.
+//   1. S^T (rows x heads) = K Q^T: q of up to 32 heads as B operands, K rows as A
+//      operands.  K and V are read from HBM in whole 256-byte rows (16 lanes per
+//      row, four rows per load): the 64-byte pieces an operand holds directly cost
+//      about 30% more time per byte read.  The wave's K rows pass through its own
+//      rows of the LDS V tile, where they are read back as operands; its V rows
+//      are written over them afterwards.
 //   2. Softmax in exp2 units against the chunk's maximum per head (wave maxima
 //      exchanged through LDS), P rounded to bf16 and written to LDS per head.
 //   3. O^T = V^T P: wave w forms the 32 columns 32w .. 32w + 31 of every head's
@@ -361,7 +364,10 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(
     int Tmax, int window, float scale, int nsplit) {
   constexpr int D = 128, NDB = D / 32, CH = kDecodeChunk;
   static_assert(CH == 128 && NDB == 4, "one 32-row block per wave, one d block per wave");
-  __shared__ __attribute__((aligned(16))) uint16_t vt[NDB * CH * 32];  // V rows, d-block-major
+  // V rows, d-block-major (dt_off layout) with blocks VP = CH + 1 rows apart: the
+  // spare 64-byte row puts the four blocks of one cache row on different banks
+  constexpr int VP = CH + 1;
+  __shared__ __attribute__((aligned(16))) uint16_t vt[NDB * VP * 32];
   __shared__ __attribute__((aligned(16))) uint16_t pt[kGqaHeads * kGqaPitch];  // P^T, per head
   __shared__ float red_m[4][kGqaHeads], red_l[4][kGqaHeads];
 
@@ -389,40 +395,39 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(
   const uint16_t *kb = kc + ((size_t)b * Tmax * Hkv + hk) * D;
   const uint16_t *vb = vc + ((size_t)b * Tmax * Hkv + hk) * D;
 
-  // K: load (u, s) reads rows 32w + 16u + l/4 in 64-byte pieces (chunks 4s .. 4s + 3,
-  // columns 32s .. 32s + 31), rows past the chunk clamped to its last row.  A lane
-  // permute then gives lane l row 16u + l % 16 and chunk 4s + l / 16: the A operand
-  // of a 16 x 16 x 32 product (row = l % 16, 8 k values per lane).  Loading the
-  // operand directly would put four adjacent 16-byte pieces in four lanes 16 apart
-  // and cost the memory pipeline 64 separate requests per load.
-  bf16x8 ka[2][NDB];
-  {
-    u32x4 raw[2][NDB];
+  // K and V rows 32w + 4j + l/16 (j = 0..7), 16-byte piece l % 16 of each, every load
+  // issued before any is used; rows past the chunk are read clamped to its last row
+  // (never used: their scores are masked, their P is 0)
+  u32x4 kraw[8], vraw[8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int r = min(32 * w + 16 * u + (lane >> 2), cnt - 1);
-      const uint16_t *kr = kb + (size_t)(t0 + r) * rs + 8 * (lane & 3);
-#pragma unroll
-      for (int s = 0; s < NDB; ++s) raw[u][s] = ldg16_stream(kr + 32 * s);
-    }
-    const int src = 4 * (4 * (lane & 15) + (lane >> 4));  // byte address of the source lane
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int s = 0; s < NDB; ++s) {
-        u32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = __builtin_amdgcn_ds_bpermute(src, raw[u][s][e]);
-        ka[u][s] = __builtin_bit_cast(bf16x8, x);
-      }
+  for (int j = 0; j < 8; ++j) {
+    const int r = min(32 * w + 4 * j + (lane >> 4), cnt - 1);
+    kraw[j] = ldg16_stream(kb + (size_t)(t0 + r) * rs + 8 * (lane & 15));
   }
-  // V: this wave's 32 rows into the tile, non-temporal (rows past the chunk clamped,
-  // never used)
 #pragma unroll
-  for (int r16 = 0; r16 < 2; ++r16)
+  for (int j = 0; j < 8; ++j) {
+    const int r = min(32 * w + 4 * j + (lane >> 4), cnt - 1);
+    vraw[j] = ldg16_stream(vb + (size_t)(t0 + r) * rs + 8 * (lane & 15));
+  }
+  // tile position of row r, 16-byte piece ch: block ch / 4, position ch % 4 ^ (r / 4) % 4
+  auto tile_at = [&](int r, int ch) {
+    return vt + (ch >> 2) * (VP * 32) + r * 32 + 8 * ((ch & 3) ^ ((r >> 2) & 3));
+  };
+  // K through the wave's own tile rows: A operand (u, s) of lane l is row 16u + l % 16,
+  // piece 4s + l / 16 (8 k values of a 16 x 16 x 32 product)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      copy_rows16<CH, 2>(vt, vb, (int)rs, t0, t0 + cnt, 32 * w + 16 * r16, db, false, lane);
+  for (int j = 0; j < 8; ++j)
+    *reinterpret_cast<u32x4 *>(tile_at(32 * w + 4 * j + (lane >> 4), lane & 15)) = kraw[j];
+  bf16x8 ka[2][NDB];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int s = 0; s < NDB; ++s)
+      ka[u][s] = lds_read_b128(tile_at(32 * w + 16 * u + (lane & 15), 4 * s + (lane >> 4)));
+  // V over them (the reads above come first: one wave's LDS accesses complete in order)
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    *reinterpret_cast<u32x4 *>(tile_at(32 * w + 4 * j + (lane >> 4), lane & 15)) = vraw[j];
 
   const float qs = scale * kLog2e;  // scores in exp2 units
   const int l16 = lane & 15, q4 = lane >> 4;
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(
         if (q4 == 0) red_m[w][16 * nt + l16] = m;
       }
     }
-    __syncthreads();  // also completes this wave's V copies before the tile is read
+    __syncthreads();  // also completes every wave's V rows before the tile is read
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       if (nt < ntile) {
@@ -500,7 +505,7 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(
     f32x16 oacc = {};
 #pragma unroll
     for (int t = 0; t < CH / 16; ++t) {
-      const bf16x8 va = dt_read_tr<CH>(vt, 16 * t, w, lane);
+      const bf16x8 va = dt_read_tr<VP>(vt, 16 * t, w, lane);
       const bf16x8 pb = lds_read_b128(pt + col * kGqaPitch + 16 * t + 8 * h);
       oacc = mfma32(va, pb, oacc);
     }
