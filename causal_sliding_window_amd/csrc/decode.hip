@@ -351,10 +351,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 // in LDS between batches.
 constexpr int kGqaHeads = 32;
 // Smallest group taken by the matrix-core kernel.  Measured on the 32-sequence
-// decode workload (H = 12): with 2 query heads per K/V head the vector-ALU kernel is
-// faster (its loads are fully coalesced and it holds no LDS tile); from 3 on the
-// matrix-core kernel is as fast or faster, 2x at 12.
-constexpr int kGqaMfmaMinGroup = 3;
+// decode workload (H = 12), cold: with 2 query heads per K/V head it takes 49.5 us
+// causal against 55.9 for the vector-ALU kernel (26.0 against 28.3 at W = 1024), and
+// the vector kernel serves the heads of a group one after another, so the gap grows
+// with the group.
+constexpr int kGqaMfmaMinGroup = 2;
 constexpr int kGqaPitch = kDecodeChunk + 8;  // P tile row pitch (bf16): rows land on distinct banks
 
 __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(

@@ -235,7 +235,7 @@ int swattn_decode_noalloc(const void *q, const void *k_cache, const void *v_cach
 /* Grouped-query decode (bf16): k_cache, v_cache [B,Tmax,Hkv,D]; each cache row is
  * read once for the H / Hkv query heads of its group.  The workspace is
  * swattn_decode_workspace_size(B, H, D, Tmax, window) bytes (partials per query
- * head); otherwise as swattn_decode.  With D = 128 and groups of 3 or more query
+ * head); otherwise as swattn_decode.  With D = 128 and groups of 2 or more query
  * heads the scores and P V run on the matrix cores, with P rounded to bf16 before
  * P V as in the forward: results then differ from the ungrouped call on repeated
  * caches by rounding only (still deterministic). */
