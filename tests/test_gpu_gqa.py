@@ -169,11 +169,11 @@ def test_gqa_decode_equals_ungrouped_on_repeated_cache(D):
         check("lse vs ungrouped", lse, f64(lse2), torch.bfloat16, lse=True)
 
 
-@pytest.mark.parametrize("H,Hkv", [(12, 4), (16, 1), (33, 1)])
+@pytest.mark.parametrize("H,Hkv", [(12, 6), (12, 4), (16, 1), (33, 1)])
 @pytest.mark.parametrize("W", [-1, 127, 128, 129, 5000])
 def test_gqa_decode_chunk_edges(H, Hkv, W):
     """Lengths on and next to the 128-row chunk edges (127, 128, 129, 256, 384 + 1) and
-    windows either side of one chunk; groups of 3, 16 and 33 query heads (the last
+    windows either side of one chunk; groups of 2, 3, 16 and 33 query heads (the last
     with a one-head second batch on the matrix-core kernel)."""
     lens = [127, 128, 129, 256, 385, 1024]
     d = inputs.decode_inputs(len(lens), H, 128, 1024, "bf16", seed=H + W, lengths=lens, Hkv=Hkv)
@@ -191,11 +191,12 @@ _EDGES = [0, 1, 2, 127, 128, 129, 255, 256, 257, 383, 384, 385, 511, 512, 513, 7
 
 
 @pytest.mark.parametrize("B,H,Hkv,Tmax,W", [(32, 24, 8, 1024, -1), (32, 12, 4, 4096, -1),
+                                            (32, 24, 12, 2048, -1),
                                             (32, 64, 2, 4096, -1), (128, 24, 8, 512, 129),
                                             (128, 24, 8, 512, 300), (64, 12, 4, 2048, 1000)])
 def test_gqa_decode_large_grids(B, H, Hkv, Tmax, W):
     """Grids of 1024 and more workgroups on the matrix-core kernel (B Hkv ceil(visible /
-    256) >= 1024): groups of 3, 12 and 32 heads, up to 128 sequences; lengths on and next
+    256) >= 1024): groups of 2, 3, 12 and 32 heads, up to 128 sequences; lengths on and next
     to the 128- and 256-row edges, an empty sequence, lengths past the window."""
     lens = [0] + [min(_EDGES[1 + i % (len(_EDGES) - 1)], Tmax) for i in range(B - 1)]
     d = inputs.decode_inputs(B, H, 128, Tmax, "bf16", seed=B + H + W, lengths=lens, Hkv=Hkv)
